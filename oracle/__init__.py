@@ -1,0 +1,14 @@
+"""CPU float64 oracle for paged KV attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the GPU library, with which it
+shares no code.
+
+Parity pins (closed forms, invariants, library special cases and brute force
+that fix each function) live in tests/test_oracle_pins.py and
+tests/test_oracle_mutants.py.  Every function here is pinned; none is
+"parity unpinned".
+"""
+
+from .paged_attention import *  # noqa: F401,F403
+from .paged_attention import __all__  # noqa: F401
