@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default workload (the one the headline metric is quoted on): one decode step
+of a Qwen3-0.6B-shaped attention layer - bf16, 16 query / 8 KV heads, head
+dim 128, KV block 16, 256 sequences with context uniform in [100, 2048] -
+i.e. the KV-cache write of the 256 new rows followed by the dispatched paged
+decode that reads them.  A "step" is that write plus that decode.
+
+Prints ONE JSON line: `value` is the step's algorithmic HBM bytes (decode
+K/V/q/out/tables + write rows) divided by the measured step time, in GB/s;
+`roofline` reports the decode kernel alone (algorithmic bytes per launch over
+its average launch time, from HIP events on the launch stream) against the
+8 TB/s HBM peak; `cpu_baseline` times the fp64 CPU oracle on the same inputs.
+
+Other workloads (--workload): `splitk` (4 x 16,384-token split-K decode),
+`mixed` (KV write + decode + ragged causal prefill in one step),
+`sweep` (single-request fp16 decode at 128 / 1,024 / 4,096 tokens, next to a
+materialise-then-attend arm), `single` (the 128-token request alone).
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts.  Pools are rotated over several device copies so no step reads what
+the previous one left in the 256 MiB Infinity Cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+ROTATE_BYTES = 1 << 30          # rotate pools until at least 1 GiB is cycled
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_step", choices=["decode_step", "splitk", "mixed", "sweep", "single"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fingerprint():
+    prop = torch.cuda.get_device_properties(0)
+    return {
+        "name": prop.name,
+        "arch": getattr(prop, "gcnArchName", ""),
+        "cus": prop.multi_processor_count,
+        "hbm_gib": round(prop.total_memory / 2**30, 1),
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+    }
+
+
+class Pools:
+    """R device copies of a step's KV pool (tables, q and new rows shared)."""
+
+    def __init__(self, step, rotate):
+        dev = torch.device("cuda:0")
+        pool_bytes = 2 * step.k_cache.numel() * step.k_cache.element_size()
+        self.R = rotate or max(2, math.ceil(ROTATE_BYTES / pool_bytes))
+        k = step.k_cache.to(dev)
+        v = step.v_cache.to(dev)
+        self.k = [k] + [k.clone() for _ in range(self.R - 1)]
+        self.v = [v] + [v.clone() for _ in range(self.R - 1)]
+        self.q = step.q.to(dev)
+        self.bt = step.block_tables.to(dev)
+        self.cl = step.context_lens.to(dev)
+        self.qsl = step.query_start_loc.to(dev)
+        self.new_k = step.new_k.to(dev) if step.new_k is not None else None
+        self.new_v = step.new_v.to(dev) if step.new_v is not None else None
+        self.slots = step.slot_mapping.to(dev) if step.slot_mapping is not None else None
+        self.out = torch.empty_like(self.q)
+
+
+def timed_loop(launch, n_phases, steps, warmup):
+    """Run `launch(i, ev)` warmup + steps times; `ev` is a list of n_phases+1
+    events the launcher records between its kernels.  Returns (wall ms per
+    step, per-phase mean ms from events)."""
+    for i in range(warmup):
+        launch(i, None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_phases + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        launch(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    phases = [sum(e[p].elapsed_time(e[p + 1]) for e in evs) / steps for p in range(n_phases)]
+    return wall_ms, phases
+
+
+def cpu_baseline_decode(step, write, budget_s):
+    """Time the oracle (as is) on the step's inputs: KV write + decode of
+    all sequences, repeated while the budget lasts (at least once)."""
+    import oracle
+
+    threads = torch.get_num_threads()
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        kc, vc = step.k_cache, step.v_cache
+        if write:
+            kc, vc = oracle.kv_cache_write(step.new_k, step.new_v, step.slot_mapping, kc, vc)
+        oracle.decode(step.decode_q, kc, vc, step.decode_block_tables, step.decode_context_lens, step.scale)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (passes + 1) / passes > 3 * budget_s:
+            break
+    per_pass = el / passes
+    nbytes = W.decode_bytes(step) + (W.kv_write_bytes(step) if write else 0)
+    return {
+        "value": round(nbytes / per_pass / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 torch-CPU oracle: {'KV write + ' if write else ''}decode of all {step.num_decode} "
+                  f"sequences, {passes} pass(es) in {el:.1f} s ({per_pass * 1e3:.0f} ms/pass), "
+                  f"{os.cpu_count()} host CPUs visible",
+        "ms_per_step": round(per_pass * 1e3, 2),
+    }
+
+
+def bench_decode_step(args, pka):
+    step = W.config_3(seed=args.seed)
+    log(f"config3: {step.num_decode} seqs, {int(step.context_lens.sum())} context tokens, pool {step.num_blocks} blocks")
+    P = Pools(step, args.rotate)
+    S, Hq, D = step.decode_q.shape
+    max_ctx = step.max_context_len
+    variant = pka.decode_choose_variant(S, step.num_kv_heads, max_ctx)
+    ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, max_ctx)), dtype=torch.uint8, device="cuda:0")
+
+    def launch(i, ev):
+        r = i % P.R
+        if ev:
+            ev[0].record()
+        pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r])
+        if ev:
+            ev[1].record()
+        pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out, workspace=ws)
+        if ev:
+            ev[2].record()
+
+    wall_ms, (write_ms, dec_ms) = timed_loop(launch, 2, args.steps, args.warmup)
+    dbytes = W.decode_bytes(step)
+    wbytes = W.kv_write_bytes(step)
+    value = (dbytes + wbytes) / (wall_ms * 1e-3) / 1e9
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(wall_ms, 4),
+        "decode_us_per_call": round(dec_ms * 1e3, 2),
+        "kv_write_us_per_call": round(write_ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "dtype": "bf16",
+        "config": {
+            "workload": "batched GQA paged decode step (KV write of 256 rows + decode), bf16, 256 seqs, "
+                        "16q/8kv heads, head_dim 128, block 16, ctx U[100,2048]",
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": step.num_kv_heads, "head_dim": D,
+            "block_size": step.block_size, "context_tokens": int(step.context_lens.sum()),
+            "max_context_len": max_ctx, "pool_blocks": step.num_blocks, "pool_copies_rotated": P.R,
+            "decode_variant": "single-pass" if variant == 1 else "split-K + reduce", "seed": args.seed,
+            "algorithmic_bytes": {"decode": dbytes, "kv_write": wbytes},
+        },
+        "roofline": {
+            "kernel": "paged_decode_kernel (single pass)" if variant == 1 else "split-K decode + reduce",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        },
+    }
+    return res, step, True
+
+
+def bench_splitk(args, pka):
+    step = W.config_4(seed=args.seed)
+    P = Pools(step, args.rotate)
+    S, Hq, D = step.decode_q.shape
+    max_ctx = step.max_context_len
+    bufs = pka.splitk_buffers(S, Hq, D, max_ctx, "cuda:0")
+
+    def launch(i, ev):
+        r = i % P.R
+        if ev:
+            ev[0].record()
+        pka.paged_attn_decode_splitk(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, *bufs)
+        if ev:
+            ev[1].record()
+        pka.paged_attn_splitk_reduce(*bufs, P.cl, P.out)
+        if ev:
+            ev[2].record()
+
+    wall_ms, (part_ms, red_ms) = timed_loop(launch, 2, args.steps, args.warmup)
+    dbytes = W.decode_bytes(step)
+    value = dbytes / (wall_ms * 1e-3) / 1e9
+    achieved = dbytes / (part_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(wall_ms, 4),
+        "splitk_partition_us": round(part_ms * 1e3, 2),
+        "splitk_reduce_us": round(red_ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "dtype": "bf16",
+        "config": {
+            "workload": "split-K paged decode, bf16, 4 seqs x 16384 ctx, 16q/8kv, head_dim 128, 256-token partitions",
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": step.num_kv_heads, "head_dim": D,
+            "context_tokens": int(step.context_lens.sum()), "pool_copies_rotated": P.R, "seed": args.seed,
+            "algorithmic_bytes": {"decode": dbytes},
+        },
+        "roofline": {
+            "kernel": "paged_decode_kernel (split-K partition pass)", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        },
+    }
+    return res, step, False
+
+
+def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
+    rows = {}
+    last = None
+    for ctx in contexts:
+        step = W.config_1(seed=args.seed) if name == "single" else W.config_2(ctx, seed=args.seed)
+        P = Pools(step, args.rotate or 2)
+        S, Hq, D = step.decode_q.shape
+        ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, ctx)), dtype=torch.uint8, device="cuda:0")
+
+        def launch(i, ev):
+            r = i % P.R
+            if ev:
+                ev[0].record()
+            pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, ctx, out=P.out, workspace=ws)
+            if ev:
+                ev[1].record()
+
+        wall_ms, (dec_ms,) = timed_loop(launch, 1, args.steps, args.warmup)
+
+        # Materialise-then-attend arm: gather the request's pages into
+        # contiguous K/V, then plain torch attention (the pages' comparison
+        # path).  Every right-hand matmul operand is made contiguous first.
+        nb = ctx // step.block_size
+        tbl = P.bt[0, :nb].long()
+        qh = P.q[0][:, None, :].contiguous()
+
+        def mat(i, ev):
+            r = i % P.R
+            if ev:
+                ev[0].record()
+            kt = P.k[r].index_select(0, tbl).reshape(ctx, step.num_kv_heads, D).permute(1, 2, 0).contiguous()
+            v = P.v[r].index_select(0, tbl).reshape(ctx, step.num_kv_heads, D).transpose(0, 1).contiguous()
+            if ev:
+                ev[1].record()
+            p = torch.softmax(torch.matmul(qh, kt).float() * step.scale, dim=-1).to(v.dtype)
+            torch.matmul(p, v)
+            if ev:
+                ev[2].record()
+
+        mwall, (gather_ms, sdpa_ms) = timed_loop(mat, 2, args.steps, args.warmup)
+        rows[str(ctx)] = {
+            "decode_us_per_call": round(dec_ms * 1e3, 2),
+            "decode_wall_us_per_call": round(wall_ms * 1e3, 2),
+            "achieved_GBps": round(W.decode_bytes(step) / (dec_ms * 1e-3) / 1e9, 2),
+            "materialise_then_attend_us": round(mwall * 1e3, 2),
+            "materialise_gather_us": round(gather_ms * 1e3, 2),
+            "variant": "single-pass" if pka.decode_choose_variant(S, step.num_kv_heads, ctx) == 1 else "split-K",
+        }
+        last = (step, dec_ms, wall_ms)
+    step, dec_ms, wall_ms = last
+    value = W.decode_bytes(step) / (wall_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "ms_per_step": round(wall_ms, 5),
+        "per_context": rows,
+        "dtype": "fp16",
+        "config": {"workload": f"single-request fp16 paged decode, 2 heads, head_dim 64, block 16, ctx {list(contexts)}",
+                   "seed": args.seed},
+        "roofline": {
+            "kernel": "paged decode (largest context)", "bound": "hbm",
+            "achieved": round(W.decode_bytes(step) / (dec_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(W.decode_bytes(step) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 6),
+            "traffic": None,
+        },
+    }
+    return res, step, False
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this library has no multi-GPU path.", flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", flush=True)
+        sys.exit(1)
+    import paged_kv_attention_21_amd as pka
+
+    torch.cuda.set_device(0)
+    if args.workload == "decode_step":
+        res, step, write = bench_decode_step(args, pka)
+    elif args.workload == "splitk":
+        res, step, write = bench_splitk(args, pka)
+    elif args.workload == "sweep":
+        res, step, write = bench_sweep(args, pka)
+    elif args.workload == "single":
+        res, step, write = bench_sweep(args, pka, contexts=(128,), name="single")
+    else:
+        raise SystemExit(f"workload {args.workload} is not available yet")
+
+    out = {
+        "metric": res.pop("metric"),
+        "value": res.pop("value"),
+        "unit": res.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": res.pop("dtype"),
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded block tables and lengths)",
+    }
+    out.update(res)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline_decode(step, write, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    out["gpu"] = fingerprint()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * pka.h - paged KV attention for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operations follow three pages on paged attention:
+ *   [MLR]  MiniLLM Runtime: "Core class relationships" (logical token ->
+ *          logical block + offset -> block table -> physical KV address) and
+ *          "CUDA PagedAttention scope" (one decode query; QK, softmax and
+ *          weighted-value accumulation read straight from paged storage).
+ *   [ME]   mini_engine: "Custom CUDA kernels" (KV-cache write with padded
+ *          slots skipped; paged prefill with online softmax over ragged
+ *          chunks that attend to earlier cached chunks; paged decode v1, one
+ *          workgroup per (sequence, KV head) with the query heads of a GQA
+ *          group sharing every K/V load; decode v2, split-K over 256-token
+ *          partitions merged by a reduce that uses each partition's saved max
+ *          and exp-sum; a dispatcher choosing between them; split attention
+ *          writing decode and prefill rows into one output tensor).
+ *   [MS]   miniserve: "Engine" flowchart (new K/V rows go to
+ *          slot = block_id * block_size + offset before attention; prefill
+ *          chunks use a bottom-right causal mask).
+ *
+ * Data layout (all tensors contiguous, row-major, in device memory that the
+ * caller owns; the library never allocates, frees or synchronises):
+ *   k_cache, v_cache   [num_blocks][block_size][num_kv_heads][head_dim]
+ *                      element type fp16 or bf16; slot s is row s of the
+ *                      flattened [num_blocks * block_size][num_kv_heads][head_dim]
+ *                      view, i.e. block s / block_size, offset s % block_size.
+ *   block_tables       int32 [num_seqs][max_blocks_per_seq]; entry [s][b] is
+ *                      the physical block holding logical tokens
+ *                      b*block_size .. b*block_size+block_size-1 of sequence s.
+ *                      Entries at or past ceil(context_len / block_size) are
+ *                      never read.
+ *   context_lens       int32 [num_seqs]: tokens sequence s attends to,
+ *                      including the current decode token or the whole
+ *                      current prefill chunk (their K/V must already be in the
+ *                      cache: write first, then attend).
+ *   q, out (decode)    [num_seqs][num_q_heads][head_dim], element type of the cache.
+ *   q, out (prefill)   [num_q_tokens][num_q_heads][head_dim]; the rows of
+ *                      sequence s are query_start_loc[s] .. query_start_loc[s+1]-1.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * scale multiplies q.k before the (natural-base) softmax.
+ * Arithmetic: fp32 accumulation; outputs rounded to nearest even.
+ *
+ * Supported shapes: block_size 16; head_dim 64 or 128;
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; fp16 or bf16.  Anything else
+ * returns PKA_ERR_UNSUPPORTED.
+ *
+ * Errors: every host-checkable problem (null pointer, bad size, unsupported
+ * shape, pointer not 16-byte aligned, workspace too small) returns a non-zero
+ * status before anything is launched.  A failed launch returns PKA_ERR_HIP.
+ * Device-data preconditions are documented and NOT checked:
+ * 0 <= block id < num_blocks for every entry that is read,
+ * 1 <= context_len <= max_blocks_per_seq * block_size,
+ * context_len <= max_context_len, query length <= context_len, and
+ * non-negative slots are distinct.  num_seqs == 0 (or num_tokens == 0) is a
+ * no-op returning PKA_OK.
+ *
+ * Streams: every call enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without waiting.
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKA_F16 = 0, PKA_BF16 = 1 } pka_dtype;
+
+typedef enum {
+  PKA_OK = 0,
+  PKA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PKA_ERR_SHAPE = 2,       /* a size is negative or sizes disagree */
+  PKA_ERR_UNSUPPORTED = 3, /* shape or dtype not built into the library */
+  PKA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  PKA_ERR_WORKSPACE = 5,   /* split-K workspace missing or too small */
+  PKA_ERR_HIP = 6          /* the HIP runtime reported an error */
+} pka_status;
+
+/* Shape of one layer's paged KV pool (k_cache and v_cache alike). */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pka_dtype */
+} pka_cache_desc;
+
+/* Split-K partition length in tokens ([ME] decode v2). */
+#define PKA_PARTITION_SIZE 256
+
+/* Human-readable name of a status code (static string). */
+const char* pka_status_str(int32_t status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pka_version(void);
+
+/*
+ * KV-cache write ([ME] KV-cache write; [MS] index_copy_ into the pool).
+ * For every i < num_tokens with slot_mapping[i] >= 0, copies key[i] into
+ * k_cache slot slot_mapping[i] and value[i] into v_cache at the same slot;
+ * rows with a negative slot are padding and are skipped.  A pure byte copy:
+ * the result is bit-exact and no other byte of the pool changes.
+ *   key, value    [num_tokens][num_kv_heads][head_dim], cache element type
+ *   slot_mapping  int64 [num_tokens]
+ */
+int32_t pka_kv_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
+                           int32_t num_tokens, void* k_cache, void* v_cache,
+                           pka_cache_desc cache, void* stream);
+
+/*
+ * Paged decode, single pass ([MLR] CUDA PagedAttention; [ME] decode v1).
+ * One query row per sequence; out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over the first context_lens[s] tokens of sequence s, K_s and V_s read in
+ * place through block_tables.  No workspace.
+ */
+int32_t pka_paged_attn_decode_v1(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 float scale, void* out, pka_cache_desc cache, void* stream);
+
+/*
+ * Split-K decode, partition pass ([ME] decode v2).  Partition p of sequence s
+ * covers logical tokens [p * partition_size, min((p + 1) * partition_size,
+ * context_lens[s])).  For each (s, h, p) with p < ceil(context_lens[s] /
+ * partition_size) it writes
+ *   max_logits[(s * num_q_heads + h) * max_num_partitions + p] = m_p
+ *       = max over the partition of scale * q . k_t
+ *   exp_sums[...same index...] = l_p = sum over the partition of exp(scale * q . k_t - m_p)
+ *   tmp_out[((s * num_q_heads + h) * max_num_partitions + p) * head_dim + d]
+ *       = sum exp(scale * q . k_t - m_p) v_t[d] / l_p            (fp32)
+ * Slots of partitions past a sequence's end are left untouched.
+ * partition_size must be PKA_PARTITION_SIZE;
+ * max_num_partitions >= ceil(max context_len / partition_size).
+ */
+int32_t pka_paged_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                     float scale, int32_t partition_size, int32_t max_num_partitions,
+                                     float* tmp_out, float* max_logits, float* exp_sums,
+                                     pka_cache_desc cache, void* stream);
+
+/*
+ * Split-K reduce ([ME] decode v2, "small reduce kernel").  For each (s, h),
+ * over the P = ceil(context_lens[s] / partition_size) partitions:
+ *   M = max_p m_p,  w_p = l_p * exp(m_p - M),
+ *   out[s][h][d] = sum_p w_p * tmp_out[..p..][d] / sum_p w_p,
+ * rounded to `dtype`.  Buffers as written by pka_paged_attn_decode_splitk.
+ */
+int32_t pka_paged_attn_splitk_reduce(const float* tmp_out, const float* max_logits,
+                                     const float* exp_sums, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t partition_size, int32_t max_num_partitions,
+                                     void* out, int32_t dtype, void* stream);
+
+/*
+ * Bytes of workspace the dispatched decode needs when it takes the split-K
+ * path: tmp_out, max_logits and exp_sums for
+ * max_num_partitions = ceil(max_context_len / PKA_PARTITION_SIZE), each
+ * region 256-byte aligned.  Pure host function.
+ */
+size_t pka_splitk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len);
+
+/*
+ * Decode dispatcher ([ME] "A dispatcher picks v2 when the batch is too small
+ * to fill the GPU (few sequences or long contexts)").  Returns 1 (single
+ * pass) or 2 (split-K) for num_seqs * num_kv_heads workgroups on num_cus
+ * compute units with contexts up to max_context_len.  Pure host function.
+ */
+int32_t pka_decode_choose_variant(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                  int32_t num_cus);
+
+/*
+ * Paged decode with dispatch: runs v1, or split-K + reduce, as
+ * pka_decode_choose_variant picks for this device.  max_context_len is a host
+ * upper bound on context_lens.  The split-K path carves its buffers from
+ * `workspace` (device memory, at least pka_splitk_workspace_bytes bytes,
+ * 256-byte aligned); the v1 path ignores it.  PKA_ERR_WORKSPACE if split-K is
+ * chosen and the workspace is missing or too small.
+ */
+int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, void* out, pka_cache_desc cache,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged prefill ([ME] paged prefill attention; [MS] bottom-right causal
+ * mask).  Ragged chunks packed in q: sequence s contributes rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 (q_len_s rows) that occupy
+ * its last q_len_s context positions; with c_s = context_lens[s] - q_len_s,
+ * row i (0-based within the chunk) attends to logical tokens 0 .. c_s + i.
+ * K and V of the chunk itself must already be in the cache.
+ * max_query_len is a host upper bound on q_len_s.  MFMA (bf16/fp16 inputs,
+ * fp32 accumulation); the softmax weights are rounded to the input type
+ * before the PV product.
+ *   query_start_loc  int32 [num_seqs + 1], query_start_loc[0] = 0,
+ *                    query_start_loc[num_seqs] = num_q_tokens
+ */
+int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs,
+                               int32_t num_q_tokens, int32_t max_query_len, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, float scale, void* out,
+                               pka_cache_desc cache, void* stream);
+
+/* Number of compute units of the current device (cached per device after the
+ * first call), or a negative value if the HIP runtime fails. */
+int32_t pka_device_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKA_H */

@@ -1,0 +1,316 @@
+"""ctypes binding of libpka.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks
+dtype / device / contiguity / shape agreement, and passes raw pointers, sizes
+and the current HIP stream to the C ABI declared in include/pka.h.  All work
+runs in the library's HIP kernels; nothing here computes attention.  If the
+library is missing, importing this module raises ImportError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpka.so")
+PARTITION_SIZE = 256
+
+c_int32 = ctypes.c_int32
+c_float = ctypes.c_float
+c_size_t = ctypes.c_size_t
+c_void_p = ctypes.c_void_p
+
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
+STATUS = {
+    0: "PKA_OK",
+    1: "PKA_ERR_NULL",
+    2: "PKA_ERR_SHAPE",
+    3: "PKA_ERR_UNSUPPORTED",
+    4: "PKA_ERR_ALIGN",
+    5: "PKA_ERR_WORKSPACE",
+    6: "PKA_ERR_HIP",
+}
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", c_int32),
+        ("block_size", c_int32),
+        ("num_kv_heads", c_int32),
+        ("head_dim", c_int32),
+        ("dtype", c_int32),
+    ]
+
+
+class PkaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+# Exported symbols: name -> (restype, argtypes)
+_SIGNATURES = {
+    "pka_status_str": (ctypes.c_char_p, [c_int32]),
+    "pka_version": (c_int32, []),
+    "pka_device_cu_count": (c_int32, []),
+    "pka_kv_cache_write": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, CacheDesc, c_void_p]),
+    "pka_paged_attn_decode_v1": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_void_p,
+         CacheDesc, c_void_p],
+    ),
+    "pka_paged_attn_decode_splitk": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, c_int32,
+         c_void_p, c_void_p, c_void_p, CacheDesc, c_void_p],
+    ),
+    "pka_paged_attn_splitk_reduce": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+         c_void_p],
+    ),
+    "pka_splitk_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "pka_decode_choose_variant": (c_int32, [c_int32, c_int32, c_int32, c_int32]),
+    "pka_paged_attn_decode": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
+         CacheDesc, c_void_p, c_size_t, c_void_p],
+    ),
+    "pka_paged_attn_prefill": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+         c_float, c_void_p, CacheDesc, c_void_p],
+    ),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_attention_21_amd.build` "
+            "(the library has no CPU fallback)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkaError(status, lib.pka_status_str(status).decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return c_void_p(t.data_ptr()) if t is not None else c_void_p(0)
+
+
+def _stream(t: torch.Tensor):
+    return c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    nb, bs, hkv, d = k_cache.shape
+    return CacheDesc(nb, bs, hkv, d, _DTYPES[k_cache.dtype])
+
+
+def _check_pool(k_cache, v_cache):
+    _require(k_cache, "k_cache", ndim=4)
+    _require(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4, device=k_cache.device)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+
+
+def _check_tables(block_tables, context_lens, num_seqs, device):
+    _require(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=device)
+    _require(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=device)
+    if block_tables.shape[0] != num_seqs or context_lens.shape[0] != num_seqs:
+        raise ValueError("block_tables / context_lens do not have one row per sequence")
+
+
+# ---------------------------------------------------------------------------
+# operations (same names as the C ABI, without the pka_ prefix)
+# ---------------------------------------------------------------------------
+
+
+def version() -> int:
+    return lib.pka_version()
+
+
+def device_cu_count() -> int:
+    n = lib.pka_device_cu_count()
+    if n <= 0:
+        raise PkaError(6, "could not query the CU count")
+    return n
+
+
+def kv_cache_write(key, value, slot_mapping, k_cache, v_cache) -> None:
+    """Scatter key/value [T, Hkv, D] into the pool at slot_mapping (int64 [T];
+    negative = skip).  Bit-exact byte copy."""
+    _check_pool(k_cache, v_cache)
+    dev = k_cache.device
+    _require(key, "key", dtype=k_cache.dtype, ndim=3, device=dev)
+    _require(value, "value", dtype=k_cache.dtype, ndim=3, device=dev)
+    _require(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1, device=dev)
+    T = key.shape[0]
+    if value.shape != key.shape or slot_mapping.shape[0] != T or key.shape[1:] != k_cache.shape[2:]:
+        raise ValueError("key/value/slot_mapping shapes disagree with each other or the pool")
+    _check(lib.pka_kv_cache_write(_ptr(key), _ptr(value), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
+                                  cache_desc(k_cache), _stream(k_cache)))
+
+
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens):
+    _check_pool(k_cache, v_cache)
+    dev = k_cache.device
+    _require(q, "q", dtype=k_cache.dtype, ndim=3, device=dev)
+    if q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the pool's")
+    _check_tables(block_tables, context_lens, q.shape[0], dev)
+
+
+def _out_like(q, out):
+    if out is None:
+        return torch.empty_like(q)
+    _require(out, "out", dtype=q.dtype, device=q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return out
+
+
+def paged_attn_decode_v1(q, k_cache, v_cache, block_tables, context_lens, scale, out=None):
+    """Single-pass paged decode: q [S, Hq, D] -> out [S, Hq, D]."""
+    _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    out = _out_like(q, out)
+    S, Hq, _ = q.shape
+    _check(lib.pka_paged_attn_decode_v1(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                        _ptr(context_lens), S, Hq, block_tables.shape[1], float(scale), _ptr(out),
+                                        cache_desc(k_cache), _stream(q)))
+    return out
+
+
+def splitk_buffers(num_seqs, num_q_heads, head_dim, max_context_len, device):
+    """Allocate (tmp_out, max_logits, exp_sums) for the split-K pass."""
+    P = -(-int(max_context_len) // PARTITION_SIZE)
+    tmp_out = torch.empty((num_seqs, num_q_heads, P, head_dim), dtype=torch.float32, device=device)
+    max_logits = torch.empty((num_seqs, num_q_heads, P), dtype=torch.float32, device=device)
+    exp_sums = torch.empty((num_seqs, num_q_heads, P), dtype=torch.float32, device=device)
+    return tmp_out, max_logits, exp_sums
+
+
+def paged_attn_decode_splitk(q, k_cache, v_cache, block_tables, context_lens, scale, tmp_out, max_logits, exp_sums,
+                             partition_size=PARTITION_SIZE):
+    """Split-K partition pass; fills tmp_out [S, Hq, P, D], max_logits and
+    exp_sums [S, Hq, P] (fp32) for every partition inside a context."""
+    _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    S, Hq, D = q.shape
+    dev = q.device
+    _require(tmp_out, "tmp_out", dtype=torch.float32, ndim=4, device=dev)
+    _require(max_logits, "max_logits", dtype=torch.float32, ndim=3, device=dev)
+    _require(exp_sums, "exp_sums", dtype=torch.float32, ndim=3, device=dev)
+    P = tmp_out.shape[2]
+    if tmp_out.shape != (S, Hq, P, D) or max_logits.shape != (S, Hq, P) or exp_sums.shape != (S, Hq, P):
+        raise ValueError("split-K buffers have the wrong shape")
+    _check(lib.pka_paged_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                            _ptr(context_lens), S, Hq, block_tables.shape[1], float(scale),
+                                            partition_size, P, _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
+                                            cache_desc(k_cache), _stream(q)))
+
+
+def paged_attn_splitk_reduce(tmp_out, max_logits, exp_sums, context_lens, out, partition_size=PARTITION_SIZE):
+    """Merge split-K partitions into out [S, Hq, D] (fp16 or bf16)."""
+    dev = out.device
+    _require(out, "out", ndim=3)
+    _require(tmp_out, "tmp_out", dtype=torch.float32, ndim=4, device=dev)
+    _require(max_logits, "max_logits", dtype=torch.float32, ndim=3, device=dev)
+    _require(exp_sums, "exp_sums", dtype=torch.float32, ndim=3, device=dev)
+    _require(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    S, Hq, P, D = tmp_out.shape
+    if out.shape != (S, Hq, D) or context_lens.shape[0] != S:
+        raise ValueError("reduce shapes disagree")
+    if out.dtype not in _DTYPES:
+        raise ValueError("out must be fp16 or bf16")
+    _check(lib.pka_paged_attn_splitk_reduce(_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _ptr(context_lens), S,
+                                            Hq, D, partition_size, P, _ptr(out), _DTYPES[out.dtype], _stream(out)))
+    return out
+
+
+def splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len) -> int:
+    return int(lib.pka_splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def decode_choose_variant(num_seqs, num_kv_heads, max_context_len, num_cus=None) -> int:
+    if num_cus is None:
+        num_cus = device_cu_count()
+    return int(lib.pka_decode_choose_variant(num_seqs, num_kv_heads, max_context_len, num_cus))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
+                      workspace=None):
+    """Paged decode with the library's dispatcher (single pass or split-K +
+    reduce).  max_context_len: host upper bound on context_lens.  workspace:
+    optional uint8 device buffer of splitk_workspace_bytes(...) bytes; one is
+    allocated when the split-K path needs it and none is given."""
+    _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    out = _out_like(q, out)
+    S, Hq, D = q.shape
+    need = splitk_workspace_bytes(S, Hq, D, max_context_len)
+    if workspace is None and decode_choose_variant(S, k_cache.shape[2], max_context_len) == 2:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+        ws_bytes = workspace.numel()
+    _check(lib.pka_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                     S, Hq, block_tables.shape[1], int(max_context_len), float(scale), _ptr(out),
+                                     cache_desc(k_cache), _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, max_query_len,
+                       out=None):
+    """Paged prefill over ragged chunks packed in q [Nq, Hq, D] (bottom-right
+    causal; chunks attend to their cached prefix).  Returns out [Nq, Hq, D]."""
+    _check_pool(k_cache, v_cache)
+    dev = k_cache.device
+    _require(q, "q", dtype=k_cache.dtype, ndim=3, device=dev)
+    S = context_lens.shape[0]
+    _check_tables(block_tables, context_lens, S, dev)
+    _require(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1, device=dev)
+    if query_start_loc.shape[0] != S + 1:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries")
+    out = _out_like(q, out)
+    Nq, Hq, _ = q.shape
+    _check(lib.pka_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                      _ptr(query_start_loc), S, Nq, int(max_query_len), Hq, block_tables.shape[1],
+                                      float(scale), _ptr(out), cache_desc(k_cache), _stream(q)))
+    return out

@@ -1,0 +1,82 @@
+"""Build libpka.so, the paged-attention C-ABI library, for gfx950.
+
+Every source under csrc/ is compiled with hipcc for gfx950 only and linked
+into one shared library next to this file.  Packed-fp32 code generation is
+switched off (-packed-fp32-ops): the compiler would otherwise fuse pairs of
+fp32 operations into v_pk_* instructions.
+
+Usage: python -m paged_kv_attention_21_amd.build   (or build() from Python).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build", "pka")
+LIB_NAME = "libpka.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; the library needs the ROCm toolchain")
+    return path
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature and says so; drop that line
+    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source and link libpka.so; returns the library path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"]
+        cmds.append([hipcc, *lang, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), os.cpu_count() or 4)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,298 @@
+// C ABI of the paged-attention library: argument checks (host only, before
+// any launch), the decode dispatcher, and the launches on the caller's stream.
+// The operations are defined in include/pka.h.
+
+#include "pka.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cu_count[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t elem_size(int32_t dtype) { return 2; }
+
+// Shape checks common to every call that reads the pool.
+int32_t check_cache(const pka_cache_desc& c) {
+  if (c.num_blocks <= 0 || c.block_size <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0) return PKA_ERR_SHAPE;
+  if (c.dtype != PKA_F16 && c.dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
+  if (c.block_size != 16) return PKA_ERR_UNSUPPORTED;
+  if (c.head_dim != 64 && c.head_dim != 128) return PKA_ERR_UNSUPPORTED;
+  return PKA_OK;
+}
+
+int32_t check_group(int32_t num_q_heads, int32_t num_kv_heads, int32_t* group) {
+  if (num_q_heads <= 0) return PKA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads) return PKA_ERR_SHAPE;
+  const int32_t g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PKA_ERR_UNSUPPORTED;
+  *group = g;
+  return PKA_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? PKA_OK : PKA_ERR_HIP; }
+
+int32_t num_partitions(int32_t max_context_len) {
+  return (max_context_len + pka::kPartitionSize - 1) / pka::kPartitionSize;
+}
+
+// Shared checks of the decode entry points; fills `a` on success.
+int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_blocks_per_seq, float scale, const pka_cache_desc& cache,
+                       pka::DecodeArgs* a) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PKA_ERR_NULL;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  int32_t group = 0;
+  st = check_group(num_q_heads, cache.num_kv_heads, &group);
+  if (st) return st;
+  if (max_blocks_per_seq <= 0) return PKA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKA_ERR_ALIGN;
+  *a = pka::DecodeArgs{};
+  a->q = static_cast<const uint16_t*>(q);
+  a->k_cache = static_cast<const uint16_t*>(k_cache);
+  a->v_cache = static_cast<const uint16_t*>(v_cache);
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->num_seqs = num_seqs;
+  a->num_kv_heads = cache.num_kv_heads;
+  a->group = group;
+  a->head_dim = cache.head_dim;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->scale = scale;
+  a->bf16 = cache.dtype == PKA_BF16;
+  return PKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pka_status_str(int32_t status) {
+  switch (status) {
+    case PKA_OK: return "ok";
+    case PKA_ERR_NULL: return "null pointer argument";
+    case PKA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case PKA_ERR_UNSUPPORTED: return "shape or dtype not supported by this library";
+    case PKA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case PKA_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PKA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t pka_version(void) { return 100; }
+
+int32_t pka_device_cu_count(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev < 0 || dev >= kMaxDevices) return -1;
+  int32_t n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return -1;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int32_t pka_kv_cache_write(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* k_cache, void* v_cache, pka_cache_desc cache, void* stream) {
+  if (num_tokens < 0) return PKA_ERR_SHAPE;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens == 0) return PKA_OK;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PKA_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache)) return PKA_ERR_ALIGN;
+  pka::KvWriteArgs a{};
+  a.key = key;
+  a.value = value;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.row_bytes = cache.num_kv_heads * cache.head_dim * elem_size(cache.dtype);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return hip_status(pka::launch_kv_write(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pka_paged_attn_decode_v1(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, void* out,
+                                 pka_cache_desc cache, void* stream) {
+  if (num_seqs < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  pka::DecodeArgs a;
+  int32_t st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                              max_blocks_per_seq, scale, cache, &a);
+  if (st) return st;
+  if (!out) return PKA_ERR_NULL;
+  if (!aligned16(out)) return PKA_ERR_ALIGN;
+  if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
+  a.out = static_cast<uint16_t*>(out);
+  return hip_status(pka::launch_decode(a, false, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pka_paged_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_blocks_per_seq, float scale,
+                                     int32_t partition_size, int32_t max_num_partitions, float* tmp_out,
+                                     float* max_logits, float* exp_sums, pka_cache_desc cache, void* stream) {
+  if (num_seqs < 0 || max_num_partitions < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  if (partition_size != pka::kPartitionSize) return PKA_ERR_UNSUPPORTED;
+  pka::DecodeArgs a;
+  int32_t st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                              max_blocks_per_seq, scale, cache, &a);
+  if (st) return st;
+  if (max_num_partitions == 0) return PKA_ERR_SHAPE;
+  if (!tmp_out || !max_logits || !exp_sums) return PKA_ERR_WORKSPACE;
+  if (num_seqs > 65535 || max_num_partitions > 65535) return PKA_ERR_UNSUPPORTED;
+  a.max_num_partitions = max_num_partitions;
+  a.tmp_out = tmp_out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  return hip_status(pka::launch_decode(a, true, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pka_paged_attn_splitk_reduce(const float* tmp_out, const float* max_logits, const float* exp_sums,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t head_dim, int32_t partition_size, int32_t max_num_partitions,
+                                     void* out, int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || max_num_partitions <= 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  if (!tmp_out || !max_logits || !exp_sums || !context_lens || !out) return PKA_ERR_NULL;
+  if (dtype != PKA_F16 && dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PKA_ERR_UNSUPPORTED;
+  if (partition_size != pka::kPartitionSize) return PKA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
+  pka::ReduceArgs a{};
+  a.tmp_out = tmp_out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.partition_size = partition_size;
+  a.max_num_partitions = max_num_partitions;
+  a.bf16 = dtype == PKA_BF16;
+  a.out = static_cast<uint16_t*>(out);
+  return hip_status(pka::launch_splitk_reduce(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pka_splitk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions(max_context_len);
+  return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+int32_t pka_decode_choose_variant(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                  int32_t num_cus) {
+  // Nothing to split in a single partition.
+  if (max_context_len <= pka::kPartitionSize) return 1;
+  if (num_cus <= 0) num_cus = 256;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  // Enough (sequence, KV head) workgroups to give every CU several, and no
+  // context so long that one workgroup's tail dominates: single pass.
+  if (units >= 4 * (int64_t)num_cus && max_context_len <= 4096) return 1;
+  return 2;
+}
+
+int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* out,
+                              pka_cache_desc cache, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_context_len < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  if (max_context_len == 0) return PKA_ERR_SHAPE;
+  pka::DecodeArgs a;
+  int32_t st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                              max_blocks_per_seq, scale, cache, &a);
+  if (st) return st;
+  if (!out) return PKA_ERR_NULL;
+  if (!aligned16(out)) return PKA_ERR_ALIGN;
+  if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
+  a.out = static_cast<uint16_t*>(out);
+  const int32_t cus = pka_device_cu_count();
+  const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len, cus);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (variant == 1) return hip_status(pka::launch_decode(a, false, s));
+
+  const int32_t P = num_partitions(max_context_len);
+  if (P > 65535) return PKA_ERR_UNSUPPORTED;
+  const size_t need = pka_splitk_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len);
+  if (!workspace || workspace_bytes < need) return PKA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKA_ERR_ALIGN;
+  const size_t rows = (size_t)num_seqs * num_q_heads * P;
+  char* w = static_cast<char*>(workspace);
+  a.max_num_partitions = P;
+  a.tmp_out = reinterpret_cast<float*>(w);
+  a.max_logits = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)));
+  a.exp_sums = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)) +
+                                        align256(rows * sizeof(float)));
+  hipError_t e = pka::launch_decode(a, true, s);
+  if (e != hipSuccess) return PKA_ERR_HIP;
+  pka::ReduceArgs r{};
+  r.tmp_out = a.tmp_out;
+  r.max_logits = a.max_logits;
+  r.exp_sums = a.exp_sums;
+  r.context_lens = context_lens;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = cache.head_dim;
+  r.partition_size = pka::kPartitionSize;
+  r.max_num_partitions = P;
+  r.bf16 = a.bf16;
+  r.out = a.out;
+  return hip_status(pka::launch_splitk_reduce(r, s));
+}
+
+int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                               int32_t num_q_tokens, int32_t max_query_len, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, float scale, void* out, pka_cache_desc cache,
+                               void* stream) {
+  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0 || num_q_tokens == 0) return PKA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc || !out)
+    return PKA_ERR_NULL;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  int32_t group = 0;
+  st = check_group(num_q_heads, cache.num_kv_heads, &group);
+  if (st) return st;
+  if (max_blocks_per_seq <= 0 || max_query_len == 0 || max_query_len > num_q_tokens) return PKA_ERR_SHAPE;
+  if (!pka::prefill_supported(cache.dtype == PKA_BF16, cache.head_dim, group)) return PKA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKA_ERR_ALIGN;
+  pka::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.max_query_len = max_query_len;
+  a.num_kv_heads = cache.num_kv_heads;
+  a.group = group;
+  a.head_dim = cache.head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  a.bf16 = cache.dtype == PKA_BF16;
+  a.out = static_cast<uint16_t*>(out);
+  return hip_status(pka::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pka {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite "minus infinity" for running maxima: exp2(m - m') stays 0 or 1 and
+// never becomes NaN when both maxima are still at their initial value.
+constexpr float kNegBig = -1.0e30f;
+
+struct F16 {};
+struct BF16 {};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Elem;
+
+// fp16: two elements per dword.  dot2 is v_dot2c_f32_f16 (fp32 accumulate).
+template <>
+struct Elem<F16> {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  }
+  // round to nearest even
+  static __device__ __forceinline__ uint16_t from_float(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+};
+
+// bf16: the upper half of an fp32.  dot2 is v_dot2c_f32_bf16.
+template <>
+struct Elem<BF16> {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), c,
+                                           false);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+  static __device__ __forceinline__ uint16_t from_float(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+};
+
+// Lane move inside a 16-lane DPP row (bound_ctrl: out-of-row reads give 0,
+// which the patterns below never do).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i within 16
+
+// Sum over aligned groups of N consecutive lanes (N in 8, 16, 32, 64);
+// every lane of a group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group of 8..64 lanes");
+  x += dpp_mov<kDppQuadSwap1>(x);
+  x += dpp_mov<kDppQuadSwap2>(x);
+  x += dpp_mov<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_mov<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+}  // namespace pka

@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pka {
+
+// Split-K partition length in tokens (one partition = 16 KV blocks).
+constexpr int kPartitionSize = 256;
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t group;  // query heads per KV head
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t max_num_partitions;  // split-K only
+  float scale;
+  bool bf16;
+  uint16_t* out;     // single pass only
+  float* tmp_out;    // split-K only
+  float* max_logits;
+  float* exp_sums;
+};
+
+struct ReduceArgs {
+  const float* tmp_out;
+  const float* max_logits;
+  const float* exp_sums;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t partition_size;
+  int32_t max_num_partitions;
+  bool bf16;
+  uint16_t* out;
+};
+
+struct KvWriteArgs {
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_bytes;  // num_kv_heads * head_dim * element size, a multiple of 16
+  void* k_cache;
+  void* v_cache;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int32_t num_seqs;
+  int32_t num_q_tokens;
+  int32_t max_query_len;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  float scale;
+  bool bf16;
+  uint16_t* out;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream);
+hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+bool prefill_supported(bool bf16, int head_dim, int group);
+
+}  // namespace pka

@@ -1,0 +1,189 @@
+"""GPU parity of paged decode (single pass, split-K + reduce, dispatcher)
+against the fp64 oracle, on the measured configs at full size and on edge
+cases.  Pools are NaN-poisoned wherever no sequence owns a slot, so any stray
+read shows up as a non-finite output."""
+
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import TOL, DevStep, assert_parity, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pka():
+    import paged_kv_attention_21_amd as pka
+
+    return pka
+
+
+def oracle_decode(step, seqs=None, k_cache=None, v_cache=None):
+    return oracle.decode(step.decode_q, step.k_cache if k_cache is None else k_cache,
+                         step.v_cache if v_cache is None else v_cache, step.decode_block_tables,
+                         step.decode_context_lens, step.scale, seqs=seqs)
+
+
+def run_decode(pka, ds, variant, max_ctx=None):
+    step = ds.step
+    S, Hq, D = ds.decode_q.shape
+    max_ctx = int(step.decode_context_lens.max()) if max_ctx is None else max_ctx
+    say(f"decode {variant} {step.name} seed={step.seed} S={S} Hq={Hq} Hkv={step.num_kv_heads} D={D} "
+        f"{step.dtype} max_ctx={max_ctx}")
+    args = (ds.decode_q, ds.k_cache, ds.v_cache, ds.decode_block_tables, ds.decode_context_lens, step.scale)
+    if variant == "auto":
+        out = pka.paged_attn_decode(*args, max_context_len=max_ctx)
+    elif variant == "v1":
+        out = pka.paged_attn_decode_v1(*args)
+    elif variant == "v2":
+        bufs = pka.splitk_buffers(S, Hq, D, max_ctx, ds.q.device)
+        pka.paged_attn_decode_splitk(*args, *bufs)
+        out = torch.empty_like(ds.decode_q)
+        pka.paged_attn_splitk_reduce(*bufs, ds.decode_context_lens, out)
+    else:
+        raise ValueError(variant)
+    torch.cuda.synchronize()
+    return out
+
+
+VARIANTS = ["auto", "v1", "v2"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_config1_single_request_fp16(pka, seed, variant):
+    step = W.config_1(seed=seed, poison=True)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), step.dtype, f"config1 seed {seed} {variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("ctx", [128, 1024, 4096])
+def test_config2_context_sweep_fp16(pka, ctx, variant):
+    step = W.config_2(ctx, seed=0, poison=True)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), step.dtype, f"config2 ctx {ctx} {variant}")
+
+
+def test_config3_write_then_decode_full(pka):
+    """The measured step at full size: KV write of 256 rows, then dispatched
+    decode over 256 sequences reading the rows just written."""
+    step = W.config_3(seed=0, poison=True)
+    ds = DevStep(step)
+    say("config3 kv_cache_write 256 rows")
+    pka.kv_cache_write(ds.new_k, ds.new_v, ds.slot_mapping, ds.k_cache, ds.v_cache)
+    torch.cuda.synchronize()
+    kc, vc = oracle.kv_cache_write(step.new_k, step.new_v, step.slot_mapping, step.k_cache, step.v_cache)
+    assert torch.equal(ds.k_cache.cpu().view(torch.int16), kc.view(torch.int16)), "K pool differs bitwise"
+    assert torch.equal(ds.v_cache.cpu().view(torch.int16), vc.view(torch.int16)), "V pool differs bitwise"
+    ref = oracle_decode(step, k_cache=kc, v_cache=vc)
+    for variant in VARIANTS:
+        out = run_decode(pka, ds, variant)
+        assert_parity(out, ref, step.dtype, f"config3 full {variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_config4_long_context_full(pka, variant):
+    step = W.config_4(seed=0, poison=True)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), step.dtype, f"config4 {variant}")
+
+
+EDGE_CTX = [1, 2, 15, 16, 17, 31, 255, 256, 257, 511, 512, 513, 1000]
+SHAPES = [
+    (torch.float16, 2, 2, 64),
+    (torch.bfloat16, 16, 8, 128),
+    (torch.float16, 8, 4, 128),
+    (torch.bfloat16, 4, 1, 64),
+    (torch.bfloat16, 8, 1, 128),
+    (torch.float16, 4, 4, 128),
+    (torch.bfloat16, 16, 4, 64),
+]
+
+
+@pytest.mark.parametrize("variant", ["v1", "v2"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{str(s[0])[6:]}-{s[1]}q{s[2]}kv-d{s[3]}" for s in SHAPES])
+def test_edge_context_lengths(pka, shape, variant):
+    dtype, hq, hkv, d = shape
+    step = W.make_decode_step(context_lens=EDGE_CTX, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                              seed=7, poison=True, pool_factor=1.3)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), dtype, f"edge lengths {shape} {variant}")
+
+
+def test_splitk_partition_state_matches_oracle(pka):
+    step = W.make_decode_step(context_lens=[1, 255, 256, 257, 700, 2049], dtype=torch.bfloat16, num_q_heads=16,
+                              num_kv_heads=8, head_dim=128, seed=8, poison=True)
+    ds = DevStep(step)
+    S, Hq, D = step.decode_q.shape
+    bufs = pka.splitk_buffers(S, Hq, D, step.max_context_len, ds.q.device)
+    for b in bufs:
+        b.fill_(float("nan"))
+    say("splitk partition state vs oracle")
+    pka.paged_attn_decode_splitk(ds.decode_q, ds.k_cache, ds.v_cache, ds.decode_block_tables, ds.decode_context_lens,
+                                 step.scale, *bufs)
+    torch.cuda.synchronize()
+    m, l, po, npart = oracle.decode_partitions(step.decode_q, step.k_cache, step.v_cache, step.decode_block_tables,
+                                               step.decode_context_lens, step.scale, 256)
+    tmp_out, max_logits, exp_sums = (b.cpu().double() for b in bufs)
+    for s in range(S):
+        P = int(npart[s])
+        assert torch.isfinite(max_logits[s, :, :P]).all()
+        assert torch.isnan(max_logits[s, :, P:]).all(), "partition past the end was written"
+        em = (max_logits[s, :, :P] - m[s, :, :P]).abs().max().item()
+        el = ((exp_sums[s, :, :P] - l[s, :, :P]).abs() / l[s, :, :P]).max().item()
+        eo = (tmp_out[s, :, :P] - po[s, :, :P]).abs().max().item()
+        say(f"seq {s} P={P}: max-logit err {em:.2e}, exp-sum rel err {el:.2e}, partial-out err {eo:.2e}")
+        assert em < 1e-4 and el < 1e-4 and eo < 1e-4
+
+
+@pytest.mark.parametrize("variant", ["v1", "v2"])
+def test_block_placement_bit_identity(pka, variant):
+    """Relabelling physical blocks (moving contents and table entries
+    together) must not change a single output bit: the summation order depends
+    only on logical positions."""
+    step = W.make_decode_step(context_lens=[17, 300, 1025, 2000], dtype=torch.bfloat16, num_q_heads=16,
+                              num_kv_heads=8, head_dim=128, seed=9, poison=True)
+    ds = DevStep(step)
+    base = run_decode(pka, ds, variant)
+    perm = torch.randperm(step.num_blocks, generator=torch.Generator().manual_seed(1))
+    kc = torch.empty_like(step.k_cache)
+    vc = torch.empty_like(step.v_cache)
+    kc[perm] = step.k_cache
+    vc[perm] = step.v_cache
+    step.k_cache, step.v_cache = kc, vc
+    step.block_tables = perm[step.block_tables.long()].to(torch.int32)
+    ds2 = DevStep(step)
+    out = run_decode(pka, ds2, variant)
+    assert torch.equal(out.cpu().view(torch.int16), base.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("variant", ["v1", "v2", "auto"])
+def test_repeat_runs_bit_identical(pka, variant):
+    step = W.make_decode_step(context_lens=[5, 513, 1999, 64], dtype=torch.float16, num_q_heads=8, num_kv_heads=4,
+                              head_dim=128, seed=10, poison=True)
+    ds = DevStep(step)
+    a = run_decode(pka, ds, variant)
+    b = run_decode(pka, ds, variant)
+    assert torch.equal(a.cpu().view(torch.int16), b.cpu().view(torch.int16))
+
+
+def test_empty_batch_is_noop(pka):
+    step = W.make_decode_step(context_lens=[16], dtype=torch.bfloat16, seed=11)
+    ds = DevStep(step)
+    q0 = ds.decode_q[:0]
+    say("decode with zero sequences")
+    out = pka.paged_attn_decode_v1(q0, ds.k_cache, ds.v_cache, ds.decode_block_tables[:0], ds.decode_context_lens[:0],
+                                   step.scale)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
+def test_tolerances_are_the_stated_ones():
+    assert TOL[torch.float16] == 2e-3 and TOL[torch.bfloat16] == 1.5e-2
