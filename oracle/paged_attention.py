@@ -125,21 +125,26 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, seqs=None) ->
     return out
 
 
-def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, seqs=None) -> torch.Tensor:
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, seqs=None,
+            rows=None) -> torch.Tensor:
     """Paged prefill over ragged chunks.  ``q [Nq, Hq, D]`` holds the chunks
     packed back to back; chunk j is rows ``query_start_loc[j]`` to
     ``query_start_loc[j+1]`` and its sequence has ``context_lens[j]`` tokens in
     the cache, the chunk's own rows being the last ones.  Returns float64
-    ``[Nq, Hq, D]`` (rows of chunks not listed in ``seqs`` are left NaN)."""
+    ``[Nq, Hq, D]``; only chunks listed in ``seqs`` and packed rows listed in
+    ``rows`` are computed (default: all), the others are left NaN."""
     Nq, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     out = torch.full((Nq, Hq, D), float("nan"), dtype=F64)
     nseq = len(query_start_loc) - 1
     chunks = range(nseq) if seqs is None else [int(s) for s in seqs]
+    wanted = None if rows is None else {int(r) for r in rows}
     for j in chunks:
         start, end = int(query_start_loc[j]), int(query_start_loc[j + 1])
         qlen = end - start
         if qlen == 0:
+            continue
+        if wanted is not None and not any(start <= r < end for r in wanted):
             continue
         ctx = int(context_lens[j])
         cached = ctx - qlen
@@ -148,6 +153,8 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sc
         K = materialize(k_cache, block_tables[j], ctx)
         V = materialize(v_cache, block_tables[j], ctx)
         for i in range(qlen):
+            if wanted is not None and start + i not in wanted:
+                continue
             n = visible_keys(cached, i)
             qi = widen(q[start + i])
             for h in range(Hq):
