@@ -241,6 +241,69 @@ def bench_splitk(args, pka):
     return res, step, False
 
 
+def bench_mixed(args, pka):
+    step = W.config_5(seed=args.seed)
+    P = Pools(step, args.rotate)
+    nd = step.num_decode
+    S, Hq, D = step.decode_q.shape
+    max_dec = int(step.decode_context_lens.max())
+    ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, max_dec)), dtype=torch.uint8, device="cuda:0")
+    qd, qp = P.q[:nd], P.q[nd:]
+    od, op = P.out[:nd], P.out[nd:]
+    btd, btp = P.bt[:nd], P.bt[nd:]
+    cld, clp = P.cl[:nd], P.cl[nd:]
+    mql = step.max_query_len
+
+    def launch(i, ev):
+        r = i % P.R
+        if ev:
+            ev[0].record()
+        pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r])
+        if ev:
+            ev[1].record()
+        pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws)
+        if ev:
+            ev[2].record()
+        pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, out=op)
+        if ev:
+            ev[3].record()
+
+    wall_ms, (write_ms, dec_ms, pre_ms) = timed_loop(launch, 3, args.steps, args.warmup)
+    dbytes = W.decode_bytes(step)
+    wbytes = W.kv_write_bytes(step)
+    pbytes = W.prefill_bytes(step)
+    flops = W.prefill_flops(step)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    value = (dbytes + wbytes + pbytes) / (wall_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(wall_ms, 4),
+        "kv_write_us_per_call": round(write_ms * 1e3, 2),
+        "decode_us_per_call": round(dec_ms * 1e3, 2),
+        "decode_GBps": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
+        "prefill_us_per_call": round(pre_ms * 1e3, 2),
+        "prefill_TFLOPs": round(tflops, 1),
+        "dtype": "bf16",
+        "config": {
+            "workload": "mixed paged step: KV write of 2048 rows, 64 decodes (ctx U[128,2048]) and ragged causal "
+                        "prefill chunks (<=512 rows) into one output, bf16, 16q/8kv, head_dim 128, budget 2048",
+            "decode_seqs": nd, "prefill_chunks": step.num_prefill, "prefill_rows": step.num_prefill_rows,
+            "chunk_q_lens": step.meta["prefill_qlen"], "chunk_cached": step.meta["prefill_cached"],
+            "pool_copies_rotated": P.R, "seed": args.seed,
+            "algorithmic": {"decode_bytes": dbytes, "kv_write_bytes": wbytes, "prefill_bytes": pbytes,
+                            "prefill_flops": flops},
+        },
+        "roofline": {
+            "kernel": "paged_prefill_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    return res, step, True
+
+
 def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
     rows = {}
     last = None
@@ -330,6 +393,8 @@ def main():
         res, step, write = bench_splitk(args, pka)
     elif args.workload == "sweep":
         res, step, write = bench_sweep(args, pka)
+    elif args.workload == "mixed":
+        res, step, write = bench_mixed(args, pka)
     elif args.workload == "single":
         res, step, write = bench_sweep(args, pka, contexts=(128,), name="single")
     else:

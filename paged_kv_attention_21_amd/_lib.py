@@ -14,7 +14,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpka.so")
+# PKA_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PKA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpka.so")
 PARTITION_SIZE = 256
 
 c_int32 = ctypes.c_int32

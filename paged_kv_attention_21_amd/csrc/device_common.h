@@ -83,6 +83,18 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef int int4v_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: data read once (the decode K/V stream)
+// should not displace reusable lines in L2 / Infinity Cache.
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const int4v_t*>(p)));
+}
+
 __device__ __forceinline__ int uniform_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Index of this wavefront in the workgroup, in a scalar register: loops and
+// branches that depend only on it compile to scalar control flow.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 
 }  // namespace pka
