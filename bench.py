@@ -50,7 +50,8 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode_step", choices=["decode_step", "splitk", "mixed", "sweep", "single"])
+    p.add_argument("--workload", default="decode_step",
+                   choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
@@ -253,6 +254,9 @@ def bench_mixed(args, pka):
     btd, btp = P.bt[:nd], P.bt[nd:]
     cld, clp = P.cl[:nd], P.cl[nd:]
     mql = step.max_query_len
+    mcl = int(step.prefill_context_lens.max())
+    pws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq,
+                                                         step.num_kv_heads, D, mcl)), dtype=torch.uint8, device="cuda:0")
 
     def launch(i, ev):
         r = i % P.R
@@ -264,7 +268,7 @@ def bench_mixed(args, pka):
         pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws)
         if ev:
             ev[2].record()
-        pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, out=op)
+        pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, mcl, out=op, workspace=pws)
         if ev:
             ev[3].record()
 
@@ -374,6 +378,36 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
     return res, step, False
 
 
+def bench_copy(args):
+    """Calibration: a plain device-to-device copy of 1 GiB (known read and
+    write bytes), the reference against which the HBM traffic counters of the
+    attention kernels are scaled."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+
+    def launch(i, ev):
+        if ev:
+            ev[0].record()
+        dst.copy_(src)
+        if ev:
+            ev[1].record()
+
+    wall_ms, (copy_ms,) = timed_loop(launch, 1, args.steps, args.warmup)
+    res = {
+        "metric": "device-to-device copy GB/s (read + write), calibration",
+        "value": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(wall_ms, 4),
+        "dtype": "u8",
+        "config": {"workload": "copy of 1 GiB (1,048,576 KiB read + 1,048,576 KiB written per launch)"},
+        "roofline": {"kernel": "torch copy", "bound": "hbm", "achieved": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(2 * n / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    return res, None, False
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -395,6 +429,8 @@ def main():
         res, step, write = bench_sweep(args, pka)
     elif args.workload == "mixed":
         res, step, write = bench_mixed(args, pka)
+    elif args.workload == "copy":
+        res, step, write = bench_copy(args)
     elif args.workload == "single":
         res, step, write = bench_sweep(args, pka, contexts=(128,), name="single")
     else:
@@ -415,7 +451,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q/K/V, seeded block tables and lengths)",
     }
     out.update(res)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and step is not None:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline_decode(step, write, args.cpu_seconds)
     else:

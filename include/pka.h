@@ -194,18 +194,29 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
  * its last q_len_s context positions; with c_s = context_lens[s] - q_len_s,
  * row i (0-based within the chunk) attends to logical tokens 0 .. c_s + i.
  * K and V of the chunk itself must already be in the cache.
- * max_query_len is a host upper bound on q_len_s.  MFMA (bf16/fp16 inputs,
- * fp32 accumulation); the softmax weights are rounded to the input type
- * before the PV product.
+ * max_query_len and max_context_len are host upper bounds on q_len_s and
+ * context_lens[s].  MFMA (bf16/fp16 inputs, fp32 accumulation); the softmax
+ * weights are rounded to the input type before the PV product.
  *   query_start_loc  int32 [num_seqs + 1], query_start_loc[0] = 0,
  *                    query_start_loc[num_seqs] = num_q_tokens
+ * Long chunks are split over several workgroups along the keys; their partial
+ * states go to `workspace` (device memory, at least
+ * pka_prefill_workspace_bytes(...) bytes, 256-byte aligned; contents need no
+ * initialisation and are scratch after the call).  When that size is 0 the
+ * workspace may be NULL.  PKA_ERR_WORKSPACE if it is needed and too small.
  */
 int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens,
                                const int32_t* query_start_loc, int32_t num_seqs,
-                               int32_t num_q_tokens, int32_t max_query_len, int32_t num_q_heads,
-                               int32_t max_blocks_per_seq, float scale, void* out,
-                               pka_cache_desc cache, void* stream);
+                               int32_t num_q_tokens, int32_t max_query_len, int32_t max_context_len,
+                               int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, void* out,
+                               pka_cache_desc cache, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes pka_paged_attn_prefill needs for these sizes (0 when no
+ * query tile can see more keys than one split holds).  Pure host function. */
+size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 
 /* Number of compute units of the current device (cached per device after the
  * first call), or a negative value if the HIP runtime fails. */

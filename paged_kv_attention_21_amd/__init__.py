@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_v1,
     paged_attn_prefill,
     paged_attn_splitk_reduce,
+    prefill_workspace_bytes,
     splitk_buffers,
     splitk_workspace_bytes,
     version,

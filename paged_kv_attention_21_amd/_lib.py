@@ -83,15 +83,16 @@ _SIGNATURES = {
     "pka_paged_attn_prefill": (
         c_int32,
         [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
-         c_float, c_void_p, CacheDesc, c_void_p],
+         c_int32, c_float, c_void_p, CacheDesc, c_void_p, c_size_t, c_void_p],
     ),
+    "pka_prefill_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
 }
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m paged_kv_attention_21_amd.build` "
+            f"{LIB_PATH} is not built; run `python paged_kv_attention_21_amd/build.py` "
             "(the library has no CPU fallback)"
         )
     lib = ctypes.CDLL(LIB_PATH)
@@ -297,10 +298,18 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ma
     return out
 
 
+def prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
+    return int(lib.pka_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len))
+
+
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, max_query_len,
-                       out=None):
+                       max_context_len, out=None, workspace=None):
     """Paged prefill over ragged chunks packed in q [Nq, Hq, D] (bottom-right
-    causal; chunks attend to their cached prefix).  Returns out [Nq, Hq, D]."""
+    causal; chunks attend to their cached prefix).  max_query_len /
+    max_context_len: host upper bounds.  workspace: optional uint8 device
+    buffer of prefill_workspace_bytes(...) bytes (allocated here when needed
+    and not given).  Returns out [Nq, Hq, D]."""
     _check_pool(k_cache, v_cache)
     dev = k_cache.device
     _require(q, "q", dtype=k_cache.dtype, ndim=3, device=dev)
@@ -310,8 +319,16 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
     if query_start_loc.shape[0] != S + 1:
         raise ValueError("query_start_loc must have num_seqs + 1 entries")
     out = _out_like(q, out)
-    Nq, Hq, _ = q.shape
+    Nq, Hq, D = q.shape
+    need = prefill_workspace_bytes(S, Nq, Hq, k_cache.shape[2], D, int(max_context_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+        ws_bytes = workspace.numel()
     _check(lib.pka_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-                                      _ptr(query_start_loc), S, Nq, int(max_query_len), Hq, block_tables.shape[1],
-                                      float(scale), _ptr(out), cache_desc(k_cache), _stream(q)))
+                                      _ptr(query_start_loc), S, Nq, int(max_query_len), int(max_context_len), Hq,
+                                      block_tables.shape[1], float(scale), _ptr(out), cache_desc(k_cache),
+                                      _ptr(workspace), ws_bytes, _stream(q)))
     return out

@@ -5,7 +5,8 @@ into one shared library next to this file.  Packed-fp32 code generation is
 switched off (-packed-fp32-ops): the compiler would otherwise fuse pairs of
 fp32 operations into v_pk_* instructions.
 
-Usage: python -m paged_kv_attention_21_amd.build   (or build() from Python).
+Usage: python paged_kv_attention_21_amd/build.py   (run by path, so the
+package - which loads the library - is not imported before it is rebuilt).
 """
 
 from __future__ import annotations

@@ -258,12 +258,22 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
   return hip_status(pka::launch_splitk_reduce(r, s));
 }
 
+size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return pka::prefill_workspace_floats(num_q_tokens, num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                       max_context_len) *
+         sizeof(float);
+}
+
 int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
-                               int32_t num_q_tokens, int32_t max_query_len, int32_t num_q_heads,
-                               int32_t max_blocks_per_seq, float scale, void* out, pka_cache_desc cache,
-                               void* stream) {
-  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0) return PKA_ERR_SHAPE;
+                               int32_t num_q_tokens, int32_t max_query_len, int32_t max_context_len,
+                               int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, void* out,
+                               pka_cache_desc cache, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_tokens < 0 || max_query_len < 0 || max_context_len < 0) return PKA_ERR_SHAPE;
   if (num_seqs == 0 || num_q_tokens == 0) return PKA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc || !out)
     return PKA_ERR_NULL;
@@ -273,8 +283,15 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   st = check_group(num_q_heads, cache.num_kv_heads, &group);
   if (st) return st;
   if (max_blocks_per_seq <= 0 || max_query_len == 0 || max_query_len > num_q_tokens) return PKA_ERR_SHAPE;
+  if (max_context_len < max_query_len) return PKA_ERR_SHAPE;
   if (!pka::prefill_supported(cache.dtype == PKA_BF16, cache.head_dim, group)) return PKA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKA_ERR_ALIGN;
+  const size_t need = pka_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, cache.num_kv_heads,
+                                                  cache.head_dim, max_context_len);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PKA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKA_ERR_ALIGN;
+  }
   pka::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -285,6 +302,7 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   a.num_seqs = num_seqs;
   a.num_q_tokens = num_q_tokens;
   a.max_query_len = max_query_len;
+  a.max_context_len = max_context_len;
   a.num_kv_heads = cache.num_kv_heads;
   a.group = group;
   a.head_dim = cache.head_dim;
@@ -292,6 +310,7 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   a.scale = scale;
   a.bf16 = cache.dtype == PKA_BF16;
   a.out = static_cast<uint16_t*>(out);
+  a.workspace = need > 0 ? static_cast<float*>(workspace) : nullptr;
   return hip_status(pka::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 

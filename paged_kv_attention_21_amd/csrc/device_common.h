@@ -93,6 +93,40 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
 
 __device__ __forceinline__ int uniform_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
+// Combine lane l with lane l ^ 16 (resp. l ^ 32) without going through LDS:
+// v_permlane16_swap / v_permlane32_swap exchange rows between two registers,
+// so swapping two copies of x leaves, in every lane, x[l] in one register and
+// x[l ^ 16] (resp. x[l ^ 32]) in the other; a symmetric combine of the two is
+// the butterfly step whichever way the rows moved.  Written as inline asm
+// (with the two wait states a VALU write needs before a permlane read)
+// because this compiler's two-result builtins hand back one register twice.
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  return a + b;
+}
+
 // Index of this wavefront in the workgroup, in a scalar register: loops and
 // branches that depend only on it compile to scalar control flow.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }

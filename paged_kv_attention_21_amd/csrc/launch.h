@@ -9,6 +9,13 @@ namespace pka {
 // Split-K partition length in tokens (one partition = 16 KV blocks).
 constexpr int kPartitionSize = 256;
 
+// Keys per prefill split: a query tile that sees more keys is spread over
+// several workgroups whose states are merged afterwards.
+#ifndef PKA_PREFILL_SPLIT_KEYS
+#define PKA_PREFILL_SPLIT_KEYS 1024
+#endif
+constexpr int kPfSplitKeys = PKA_PREFILL_SPLIT_KEYS;
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k_cache;
@@ -63,6 +70,7 @@ struct PrefillArgs {
   int32_t num_seqs;
   int32_t num_q_tokens;
   int32_t max_query_len;
+  int32_t max_context_len;
   int32_t num_kv_heads;
   int32_t group;
   int32_t head_dim;
@@ -70,6 +78,7 @@ struct PrefillArgs {
   float scale;
   bool bf16;
   uint16_t* out;
+  float* workspace;  // split states; may be null when no tile needs more than one split
 };
 
 hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream);
@@ -77,5 +86,7 @@ hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(bool bf16, int head_dim, int group);
+size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
+                                int max_context_len);
 
 }  // namespace pka

@@ -8,11 +8,24 @@
 // table, softmax is online (running max / exp-sum per row), one launch covers
 // every chunk of the batch.
 //
-// Tiling.  A workgroup (4 wavefronts) owns 128 "q-rows" of one chunk and one
-// KV head: 128 / G query positions times the G query heads of the GQA group,
-// so every K/V tile it stages serves all G heads.  It walks the visible keys
-// in tiles of 32 (two KV blocks), staged in LDS: K row-major, V transposed.
-// Each wavefront owns 32 q-rows (two 16-row MFMA tiles).
+// Work items.  A query tile is 128 "q-rows" of one chunk and one KV head:
+// 128 / G query positions times the G query heads of the GQA group, so every
+// K/V tile staged in LDS serves all G heads.  The keys a query tile can see,
+// [0, kend), are cut into splits of kPfSplitKeys; one workgroup (4 wavefronts)
+// takes one (KV head, query tile, split).  A tile with one split writes its
+// output directly; otherwise every split leaves its unnormalised state (row
+// max, exp-sum, O) in the workspace and a merge kernel combines them with the
+// same max / exp-sum rule as the split-K decode.  Long chunks after a long
+// cached prefix - the expensive ones - thereby spread over many compute units.
+// Grid x is the KV head, so with 8 KV heads every tile of one head lands on the
+// same XCD (workgroups are dealt to the 8 XCDs round robin) and its K/V tiles
+// are shared through that XCD's L2.
+//
+// Inside a split the workgroup walks 32-key tiles (two KV blocks), staged in
+// LDS row-major (K and V alike) from registers loaded one tile ahead; the
+// split's block-table entries are staged in LDS first so no load waits on a
+// table read, and each tile's two block bases are wavefront-uniform (scalar
+// registers).  Each wavefront owns 32 q-rows (two 16-row MFMA tiles).
 //
 // Products (v_mfma_f32_16x16x32, fp32 accumulate):
 //   S^T = K Q^T : A = 16 keys x 32 dims of K (LDS), B = Q^T fragment kept in
@@ -20,11 +33,12 @@
 //                 lane 4 keys of one q-row - exactly the lane's share of the
 //                 B operand of the next product, so the softmax weights never
 //                 leave registers.
-//   O^T += V^T P^T : A = 16 dims x 32 keys of V^T (LDS), B = P^T (registers,
+//   O^T += V^T P^T : A = 16 dims x 32 keys of V^T, read from the row-major V
+//                 tile with gfx950's transposing LDS read; B = P^T (registers,
 //                 rounded to the input type).
 // Both products only need the two operands to agree on which K index each
 // (lane group, element) holds; the key order inside a tile is permuted so the
-// 8 keys a lane needs in PV are 8 consecutive rows of V^T (one 16-byte LDS read).
+// 8 keys a lane needs in PV are 8 consecutive keys (two transposing reads).
 //
 // Numerics: logits in fp32, softmax in base 2 with scale * log2 e folded in,
 // masked keys selected out (-inf logit; K/V rows past the context are zeroed in
@@ -67,22 +81,38 @@ struct Mfma<F16> {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 128;          // q-rows per workgroup (positions x group heads)
+constexpr int kPfRows = 128;          // q-rows per query tile (positions x group heads)
 constexpr int kPfRowsPerWave = 32;    // two 16-row MFMA tiles
 constexpr int kPfKeys = 32;           // keys per staged tile (two KV blocks)
 constexpr int kPfBlock = 16;          // KV block size
+constexpr int kPfSplitBlocks = kPfSplitKeys / kPfBlock;
+constexpr float kPfSlack = 8.f;       // log2 growth of a row max tolerated before rescaling
 
 template <int D>
 struct PfLds {
-  static constexpr int KROW = D + 8;         // K tile row stride (elements)
-  static constexpr int VROW = kPfKeys + 8;   // V^T tile row stride (elements)
-  static constexpr int KELEMS = kPfKeys * KROW;
-  static constexpr int VELEMS = D * VROW;
-  static constexpr int STAGE = KELEMS + VELEMS;
+  static constexpr int ROW = D + 8;          // K and V tile row stride (elements), 16-byte aligned rows
+  static constexpr int TILE = kPfKeys * ROW;  // one [32 keys][D] tile
+  static constexpr int STAGE = 2 * TILE;      // K tile, then V tile
 };
 
-// Find the chunk and the query tile of workgroup `tile` (tiles of `bq`
-// positions, numbered chunk by chunk).  Every wavefront runs the same scan.
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// output lane i gets element i % 4 of the 8-byte pieces read by input lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.  So when input lane L of group g
+// reads row 8g + L / 4, columns 4 (L % 4) .. +3 of a row-major [key][dim]
+// tile, output lane i holds keys 8g .. 8g + 3 of dim i: a column of V, i.e.
+// four K-elements of the V^T MFMA operand.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  const auto r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Bytes of one split's saved state: O[128][D], then row max[128], exp-sum[128] (fp32).
+__host__ __device__ constexpr size_t pf_slot_floats(int D) { return (size_t)kPfRows * (D + 2); }
+
+// Find the chunk and the query tile of global tile index `tile` (tiles of
+// `bq` positions, numbered chunk by chunk).  Every wavefront runs the same scan.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, int num_seqs, int bq, int tile,
                                           int* seq, int* qtile) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -114,42 +144,64 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, int n
   return false;
 }
 
+// Geometry of one query tile, shared by the attention and merge kernels.
+struct PfTile {
+  int seq, qt, qstart, qlen, cached, q0, kend, nsplit;
+};
+
+__device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
+                                        int num_seqs, int bq, int tile, PfTile* t) {
+  if (!find_tile(qsl, num_seqs, bq, tile, &t->seq, &t->qt)) return false;
+  t->qstart = qsl[t->seq];
+  t->qlen = qsl[t->seq + 1] - t->qstart;
+  t->cached = context_lens[t->seq] - t->qlen;
+  t->q0 = t->qt * bq;
+  t->kend = t->cached + t->q0 + min(bq, t->qlen - t->q0);  // keys [0, kend) are visible to some row
+  t->nsplit = (t->kend + kPfSplitKeys - 1) / kPfSplitKeys;
+  return true;
+}
+
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kPfThreads)
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
-                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads, float scale_log2,
-                     uint16_t* __restrict__ out) {
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t max_splits,
+                     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ partial) {
   using MM = Mfma<T>;
   using LD = PfLds<D>;
-  constexpr int BQ = kPfRows / G;     // query positions per workgroup
+  constexpr int BQ = kPfRows / G;     // query positions per tile
   constexpr int KSTEPS = D / 32;      // MFMA k-steps of QK^T
   constexpr int DTILES = D / 16;      // 16-dim tiles of the output
   constexpr int NT = kPfRowsPerWave / 16;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
+  __shared__ int s_tbl[kPfSplitBlocks];
 
   const int kvh = blockIdx.x;
-  int seq, qt;
-  if (!find_tile(query_start_loc, num_seqs, BQ, blockIdx.y, &seq, &qt)) return;
+  const int split = blockIdx.z;
+  PfTile tl;
+  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, blockIdx.y, &tl)) return;
+  if (split >= tl.nsplit) return;  // this tile sees fewer keys
+  if (tl.nsplit > max_splits) return;  // context longer than max_context_len: precondition broken
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_id();
   const int l16 = lane & 15;
   const int blk = lane >> 4;
   const int num_q_heads = num_kv_heads * G;
-
-  const int qstart = query_start_loc[seq];
-  const int qlen = query_start_loc[seq + 1] - qstart;
-  const int ctx = context_lens[seq];
-  const int cached = ctx - qlen;
-  const int q0 = qt * BQ;
-  const int nvalid = min(BQ, qlen - q0);
-  const int kend = cached + q0 + nvalid;  // keys [0, kend) are visible to some row
-  const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
-  const int32_t* tbl = block_tables + (size_t)seq * max_blocks_per_seq;
+  const int ctx = tl.cached + tl.qlen;
+  const int k_lo = split * kPfSplitKeys;
+  const int k_hi = min(tl.kend, k_lo + kPfSplitKeys);
+  const int ntiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
   const size_t row_elems = (size_t)num_kv_heads * D;
+
+  // Block-table entries of this split (only entries inside the context are read).
+  {
+    const int b = threadIdx.x;
+    const int lb = k_lo / kPfBlock + b;
+    if (b < kPfSplitBlocks && lb * kPfBlock < ctx) s_tbl[b] = block_tables[(size_t)tl.seq * max_blocks_per_seq + lb];
+  }
 
   // Q^T fragments (B operand): q-row n of this lane in tile nt, dims 32s + 8blk .. +7.
   uint4 qf[NT][KSTEPS];
@@ -157,79 +209,69 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = wave * kPfRowsPerWave + nt * 16 + l16;
-    const int pos = q0 + n / G;
+    const int pos = tl.q0 + n / G;
     const int g = n % G;
-    pos_of[nt] = pos < qlen ? pos : -1;
-    const uint16_t* qp = q + ((size_t)(qstart + pos) * num_q_heads + kvh * G + g) * D + 8 * blk;
+    pos_of[nt] = pos < tl.qlen ? pos : -1;
+    const uint16_t* qp = q + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + g) * D + 8 * blk;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos < qlen) v = *reinterpret_cast<const uint4*>(qp + 32 * s);
+      if (pos < tl.qlen) v = *reinterpret_cast<const uint4*>(qp + 32 * s);
       qf[nt][s] = v;
     }
   }
+  __syncthreads();  // s_tbl
 
-  // ---- global -> register staging of one key tile ----
-  constexpr int KCHUNKS = kPfKeys * D / 8;                  // 16-byte pieces of the K tile
-  constexpr int KPER = (KCHUNKS + kPfThreads - 1) / kPfThreads;
-  constexpr int VITEMS = (kPfKeys / 4) * (D / 4);            // 4 keys x 4 dims items of the V tile
-  static_assert(VITEMS <= kPfThreads, "one V item per thread");
-  uint4 kreg[KPER];
-  uint2 vreg[4];
-
-  auto row_ptr = [&](const uint16_t* cache, int key) -> const uint16_t* {
-    const int pb = tbl[key / kPfBlock];
-    return cache + ((size_t)pb * kPfBlock + key % kPfBlock) * row_elems + (size_t)kvh * D;
-  };
+  // ---- global -> register -> LDS staging of one key tile ----
+  // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (256 / (D/8)),
+  // r < PER, for K and for V alike.  With D = 128 piece set r lies in KV block r;
+  // with D = 64 it lies in block (wave / 2): the block is wavefront-uniform,
+  // so its base address sits in scalar registers and each load adds a
+  // per-lane 32-bit offset.
+  constexpr int CHUNKS = kPfKeys * D / 8;             // 16-byte pieces per tile
+  constexpr int PER = CHUNKS / kPfThreads;
+  static_assert(CHUNKS % kPfThreads == 0, "whole passes over the tile");
+  constexpr int ROWS_PER_PASS = kPfThreads / (D / 8);
+  uint4 kreg[PER], vreg[PER];
+  const int my_row = threadIdx.x / (D / 8);           // row of pass 0
+  const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
+  const uint32_t goff = (uint32_t)((my_row % kPfBlock) * row_elems + (size_t)kvh * D + my_col);  // elements
+  const size_t blk_elems = (size_t)kPfBlock * row_elems;
+  // A block past the context is replaced by the context's last block: its
+  // rows are fetched from memory the sequence owns and then zeroed.
+  const int last_blk = (ctx - 1) / kPfBlock - k_lo / kPfBlock;  // last s_tbl entry inside the context
 
   auto fetch = [&](int tile) {
-    const int k0 = tile * kPfKeys;
+    const int k0 = k_lo + tile * kPfKeys;
+    const int b0 = (k0 - k_lo) / kPfBlock;
+    const int pb0 = __builtin_amdgcn_readfirstlane(s_tbl[b0]);
+    const int pb1 = __builtin_amdgcn_readfirstlane(s_tbl[min(b0 + 1, last_blk)]);
 #pragma unroll
-    for (int r = 0; r < KPER; ++r) {
-      const int c = threadIdx.x + r * kPfThreads;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < KCHUNKS) {
-        const int key = k0 + c / (D / 8);
-        if (key < ctx) v = *reinterpret_cast<const uint4*>(row_ptr(k_cache, key) + (c % (D / 8)) * 8);
-      }
-      kreg[r] = v;
+    for (int r = 0; r < PER; ++r) {
+      const int blk_of = (my_row + r * ROWS_PER_PASS) / kPfBlock;  // 0 or 1, wavefront-uniform
+      const size_t pb = blk_of == 0 ? (size_t)pb0 : (size_t)pb1;
+      kreg[r] = *reinterpret_cast<const uint4*>(k_cache + pb * blk_elems + goff);
+      vreg[r] = *reinterpret_cast<const uint4*>(v_cache + pb * blk_elems + goff);
     }
-    const int t = threadIdx.x;
-    if (t < VITEMS) {
-      const int dg = t % (D / 4), kg = t / (D / 4);
+    if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * kg + r;
-        uint2 v = make_uint2(0, 0);
-        if (key < ctx) v = *reinterpret_cast<const uint2*>(row_ptr(v_cache, key) + 4 * dg);
-        vreg[r] = v;
+      for (int r = 0; r < PER; ++r) {
+        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) {
+          kreg[r] = make_uint4(0, 0, 0, 0);
+          vreg[r] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
   };
 
   auto stage = [&](int buf) {
     uint16_t* ks = lds + buf * LD::STAGE;
-    uint16_t* vt = ks + LD::KELEMS;
+    uint16_t* vs = ks + LD::TILE;
 #pragma unroll
-    for (int r = 0; r < KPER; ++r) {
-      const int c = threadIdx.x + r * kPfThreads;
-      if (c < KCHUNKS) *reinterpret_cast<uint4*>(ks + (c / (D / 8)) * LD::KROW + (c % (D / 8)) * 8) = kreg[r];
-    }
-    const int t = threadIdx.x;
-    if (t < VITEMS) {
-      const int dg = t % (D / 4), kg = t / (D / 4);
-      // 4 keys x 4 dims -> for each dim, the 4 keys side by side (V^T row).
-      const uint32_t a0 = vreg[0].x, a1 = vreg[0].y, b0 = vreg[1].x, b1 = vreg[1].y;
-      const uint32_t c0 = vreg[2].x, c1 = vreg[2].y, d0 = vreg[3].x, d1 = vreg[3].y;
-      const uint2 col0 = make_uint2((a0 & 0xffffu) | (b0 << 16), (c0 & 0xffffu) | (d0 << 16));
-      const uint2 col1 = make_uint2((a0 >> 16) | (b0 & 0xffff0000u), (c0 >> 16) | (d0 & 0xffff0000u));
-      const uint2 col2 = make_uint2((a1 & 0xffffu) | (b1 << 16), (c1 & 0xffffu) | (d1 << 16));
-      const uint2 col3 = make_uint2((a1 >> 16) | (b1 & 0xffff0000u), (c1 >> 16) | (d1 & 0xffff0000u));
-      uint16_t* dst = vt + (4 * dg) * LD::VROW + 4 * kg;
-      *reinterpret_cast<uint2*>(dst) = col0;
-      *reinterpret_cast<uint2*>(dst + LD::VROW) = col1;
-      *reinterpret_cast<uint2*>(dst + 2 * LD::VROW) = col2;
-      *reinterpret_cast<uint2*>(dst + 3 * LD::VROW) = col3;
+    for (int r = 0; r < PER; ++r) {
+      const int off = (my_row + r * ROWS_PER_PASS) * LD::ROW + my_col;
+      *reinterpret_cast<uint4*>(ks + off) = kreg[r];
+      *reinterpret_cast<uint4*>(vs + off) = vreg[r];
     }
   };
 
@@ -253,8 +295,8 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     if (tile + 1 < ntiles) fetch(tile + 1);
     const uint16_t* ks = lds + buf * LD::STAGE;
-    const uint16_t* vt = ks + LD::KELEMS;
-    const int k0 = tile * kPfKeys;
+    const uint16_t* vs = ks + LD::TILE;
+    const int k0 = k_lo + tile * kPfKeys;
 
     // S^T = K Q^T for both key halves and both q-row tiles.
     floatx4_t sacc[NT][2];
@@ -264,20 +306,20 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + (krow0 + 4 * kt) * LD::KROW + 32 * s + 8 * blk);
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + (krow0 + 4 * kt) * LD::ROW + 32 * s + 8 * blk);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = MM::mma(a, qf[nt][s], sacc[nt][kt]);
       }
     }
 
     // Online softmax per q-row; this lane holds keys 8*blk + 4*kt + i.
-    const bool diag = k0 + kPfKeys - 1 > cached + q0;  // some key of the tile is past some row's limit
+    const bool diag = k0 + kPfKeys - 1 > tl.cached + tl.q0;  // some key of the tile is past some row's limit
     uint4 pf[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float sv[2][4];
       float mx = kNegBig;
-      const int limit = pos_of[nt] >= 0 ? cached + pos_of[nt] : -1;  // last visible key of this q-row
+      const int limit = pos_of[nt] >= 0 ? tl.cached + pos_of[nt] : -1;  // last visible key of this q-row
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -287,47 +329,68 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           sv[kt][i] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nt], mx);
-      const float alpha = fast_exp2(m[nt] - mnew);
-      m[nt] = mnew;
+      mx = xor32_max(xor16_max(mx));
+      // Lazy rescale: the reference max only moves when some row's max grows
+      // by more than kPfSlack (log2 units), so the accumulators (kept in
+      // AGPRs) are rescaled on a handful of tiles instead of on every one;
+      // weights stay below 2^kPfSlack, harmless for fp32 sums and the
+      // bf16/fp16 rounding of P (relative).
+      if (__ballot(mx > m[nt] + kPfSlack)) {
+        const float mnew = fmaxf(m[nt], mx);
+        const float alpha = fast_exp2(m[nt] - mnew);
+        m[nt] = mnew;
+        lpart[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] *= alpha;
+      }
       float ps = 0.f;
       float p[2][4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[kt][i] = fast_exp2(sv[kt][i] - mnew);
+          p[kt][i] = fast_exp2(sv[kt][i] - m[nt]);
           ps += p[kt][i];
         }
-      lpart[nt] = lpart[nt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] *= alpha;
+      lpart[nt] += ps;
       pf[nt] = make_uint4(MM::pack2(p[0][0], p[0][1]), MM::pack2(p[0][2], p[0][3]), MM::pack2(p[1][0], p[1][1]),
                           MM::pack2(p[1][2], p[1][3]));
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; the V^T operand (dims 16 dt + l16, keys 8 blk .. +7) comes
+    // from the row-major V tile through two transposing reads.
+    const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 4 * (l16 & 3);
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      const uint4 a = *reinterpret_cast<const uint4*>(vt + (16 * dt + l16) * LD::VROW + 8 * blk);
+      const uint2 lo = lds_read_tr16(vrd + 16 * dt);
+      const uint2 hi = lds_read_tr16(vrd + 4 * LD::ROW + 16 * dt);
+      const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt][dt] = MM::mma(a, pf[nt], o[nt][dt]);
     }
   }
 
-  // Normalise and store: lane holds dims 16*dt + 4*blk + i of q-row l16 of tile nt.
+  // Lane holds dims 16*dt + 4*blk + i of q-row l16 of tile nt.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float lt = lpart[nt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xor32_sum(xor16_sum(lpart[nt]));
+    const int n = wave * kPfRowsPerWave + nt * 16 + l16;
+    if (tl.nsplit > 1) {
+      // Unnormalised state of this split for the merge (invalid rows too: they are never stored).
+      float* slot = partial + (((size_t)blockIdx.y * max_splits + split) * num_kv_heads + kvh) * pf_slot_floats(D);
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+        *reinterpret_cast<floatx4_t*>(slot + (size_t)n * D + 16 * dt + 4 * blk) = o[nt][dt];
+      if (blk == 0) {
+        slot[(size_t)kPfRows * D + n] = m[nt];
+        slot[(size_t)kPfRows * D + kPfRows + n] = lt;
+      }
+      continue;
+    }
     if (pos_of[nt] < 0) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int n = wave * kPfRowsPerWave + nt * 16 + l16;
     const int g = n % G;
-    uint16_t* op = out + ((size_t)(qstart + pos_of[nt]) * num_q_heads + kvh * G + g) * D + 4 * blk;
+    uint16_t* op = out + ((size_t)(tl.qstart + pos_of[nt]) * num_q_heads + kvh * G + g) * D + 4 * blk;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
       const floatx4_t v = o[nt][dt] * inv;
@@ -336,15 +399,79 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 }
 
+// Merge the splits of every query tile that has more than one: per q-row,
+// M = max_s m_s, w_s = exp2(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s.
+// Two threads per q-row, each owning half of its dims, so the weights are
+// computed twice per row and every O load is an independent 16-byte read.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kPfThreads)
+paged_prefill_merge_kernel(const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
+                           int32_t num_seqs, int32_t num_kv_heads, int32_t max_splits,
+                           const float* __restrict__ partial, uint16_t* __restrict__ out) {
+  static_assert(kPfThreads == 2 * kPfRows, "two threads per q-row");
+  constexpr int BQ = kPfRows / G;
+  constexpr int HALF = D / 2;
+  const int kvh = blockIdx.x;
+  PfTile tl;
+  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, blockIdx.y, &tl)) return;
+  if (tl.nsplit <= 1 || tl.nsplit > max_splits) return;
+  const int n = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const int pos = tl.q0 + n / G;
+  if (pos >= tl.qlen) return;
+  const int num_q_heads = num_kv_heads * G;
+  const size_t slot_stride = (size_t)num_kv_heads * pf_slot_floats(D);
+  const float* base = partial + ((size_t)blockIdx.y * max_splits * num_kv_heads + kvh) * pf_slot_floats(D);
+  float mm = kNegBig;
+  for (int s = 0; s < tl.nsplit; ++s) mm = fmaxf(mm, base[s * slot_stride + (size_t)kPfRows * D + n]);
+  float lt = 0.f;
+  floatx4_t acc[HALF / 4];
+#pragma unroll
+  for (int c = 0; c < HALF / 4; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < tl.nsplit; ++s) {
+    const float* sl = base + s * slot_stride;
+    const float w = fast_exp2(sl[(size_t)kPfRows * D + n] - mm);
+    lt += w * sl[(size_t)kPfRows * D + kPfRows + n];
+    const floatx4_t* po = reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + half * HALF);
+#pragma unroll
+    for (int c = 0; c < HALF / 4; ++c) acc[c] += w * po[c];
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  uint16_t* op = out + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + half * HALF;
+#pragma unroll
+  for (int c = 0; c < HALF / 8; ++c) {
+    const floatx4_t a = acc[2 * c] * inv, b = acc[2 * c + 1] * inv;
+    *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(Mfma<T>::pack2(a[0], a[1]), Mfma<T>::pack2(a[2], a[3]),
+                                                       Mfma<T>::pack2(b[0], b[1]), Mfma<T>::pack2(b[2], b[3]));
+  }
+}
+
+size_t prefill_tiles_upper_bound(int num_q_tokens, int num_seqs, int group) {
+  const int bq = kPfRows / group;
+  return (size_t)(num_q_tokens + bq - 1) / bq + num_seqs;
+}
+
+size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
+                                int max_context_len) {
+  const size_t splits = (size_t)(max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
+  if (splits <= 1) return 0;
+  return prefill_tiles_upper_bound(num_q_tokens, num_seqs, group) * splits * num_kv_heads * pf_slot_floats(head_dim);
+}
+
 template <typename T, int D, int G>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  constexpr int BQ = kPfRows / G;
-  const long long tiles = (long long)(a.num_q_tokens + BQ - 1) / BQ + a.num_seqs;
-  if (tiles > 65535) return hipErrorInvalidValue;
-  dim3 grid(a.num_kv_heads, (unsigned)tiles);
+  const size_t tiles = prefill_tiles_upper_bound(a.num_q_tokens, a.num_seqs, G);
+  const int splits = (a.max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
+  if (tiles > 65535 || splits > 65535) return hipErrorInvalidValue;
+  dim3 grid(a.num_kv_heads, (unsigned)tiles, (unsigned)splits);
   hipLaunchKernelGGL((paged_prefill_kernel<T, D, G>), grid, dim3(kPfThreads), 0, stream, a.q, a.k_cache, a.v_cache,
                      a.block_tables, a.context_lens, a.query_start_loc, a.num_seqs, a.max_blocks_per_seq,
-                     a.num_kv_heads, a.scale * kLog2e, a.out);
+                     a.num_kv_heads, splits, a.scale * kLog2e, a.out, a.workspace);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits <= 1) return e;
+  hipLaunchKernelGGL((paged_prefill_merge_kernel<T, D, G>), dim3(a.num_kv_heads, (unsigned)tiles), dim3(kPfThreads),
+                     0, stream, a.context_lens, a.query_start_loc, a.num_seqs, a.num_kv_heads, splits, a.workspace,
+                     a.out);
   return hipGetLastError();
 }
 

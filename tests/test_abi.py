@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     syms = _declared_symbols()
     for name in ("pka_kv_cache_write", "pka_paged_attn_decode", "pka_paged_attn_decode_v1",
                  "pka_paged_attn_decode_splitk", "pka_paged_attn_splitk_reduce", "pka_paged_attn_prefill",
-                 "pka_splitk_workspace_bytes", "pka_decode_choose_variant", "pka_status_str"):
+                 "pka_splitk_workspace_bytes", "pka_decode_choose_variant", "pka_status_str",
+                 "pka_prefill_workspace_bytes"):
         assert name in syms
 
 
@@ -98,11 +99,17 @@ def test_prefill_validation(pka):
     lib = pka._lib.lib
     d = _desc(pka, hkv=8, d=128, dt=1)
     pf = lib.pka_paged_attn_prefill
-    assert pf(A, A, A, A, A, A, 0, 0, 0, 16, 8, 0.1, A, d, None) == 0
-    assert pf(A, A, A, A, A, None, 2, 10, 5, 16, 8, 0.1, A, d, None) == 1
-    assert pf(A, A, A, A, A, A, 2, 10, 11, 16, 8, 0.1, A, d, None) == 2  # max_query_len > num_q_tokens
-    assert pf(A, A, A, A, A, A, 2, 10, 5, 12, 8, 0.1, A, d, None) == 2   # 12 % 8
-    assert pf(A, A, A, A, A, A, 2, 10, 5, 16, 8, 0.1, A, _desc(pka, bs=32, hkv=8, d=128, dt=1), None) == 3
+    assert pf(A, A, A, A, A, A, 0, 0, 0, 0, 16, 8, 0.1, A, d, None, 0, None) == 0
+    assert pf(A, A, A, A, A, None, 2, 10, 5, 100, 16, 8, 0.1, A, d, None, 0, None) == 1
+    assert pf(A, A, A, A, A, A, 2, 10, 11, 100, 16, 8, 0.1, A, d, None, 0, None) == 2  # max_query_len > num_q_tokens
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 4, 16, 8, 0.1, A, d, None, 0, None) == 2     # max_context_len < max_query_len
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 12, 8, 0.1, A, d, None, 0, None) == 2   # 12 % 8
+    bad = _desc(pka, bs=32, hkv=8, d=128, dt=1)
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, bad, None, 0, None) == 3
+    # a tile can see more keys than one split holds: the workspace is required
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 5000, 16, 8, 0.1, A, d, None, 0, None) == 5
+    need = pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 5000)
+    assert need > 0 and pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 1024) == 0
 
 
 def test_workspace_bytes_and_dispatcher(pka):

@@ -26,7 +26,8 @@ def run_prefill(pka, ds, out=None):
         f"Hq={step.num_q_heads} Hkv={step.num_kv_heads} D={step.head_dim} {step.dtype} "
         f"qlen={step.meta['prefill_qlen']} cached={step.meta['prefill_cached']}")
     out = pka.paged_attn_prefill(ds.prefill_q, ds.k_cache, ds.v_cache, ds.prefill_block_tables,
-                                 ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len, out=out)
+                                 ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len,
+                                 int(step.prefill_context_lens.max()), out=out)
     torch.cuda.synchronize()
     return out
 
@@ -60,6 +61,21 @@ def test_ragged_chunks(pka, shape):
     ds = DevStep(step)
     out = run_prefill(pka, ds)
     assert_parity(out, oracle_prefill(step), dtype, f"ragged prefill {shape}")
+
+
+@pytest.mark.parametrize("shape", [(torch.bfloat16, 16, 8, 128), (torch.float16, 8, 8, 64)],
+                         ids=["bf16-16q8kv-d128", "fp16-8q8kv-d64"])
+def test_long_context_splits(pka, shape):
+    """Query tiles whose visible keys cross one or more key-split boundaries
+    (1,024 keys): exactly at a boundary, one past it, several splits, and a
+    single row after a 7,679-token prefix."""
+    dtype, hq, hkv, d = shape
+    step = W.make_prefill_step(query_lens=[64, 65, 128, 1, 300, 17], cached_lens=[960, 960, 3000, 7679, 2500, 1023],
+                               dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seed=36, poison=True,
+                               write_new=False)
+    ds = DevStep(step)
+    out = run_prefill(pka, ds)
+    assert_parity(out, oracle_prefill(step), dtype, f"long-context splits {shape}")
 
 
 def test_shared_prefix_chunks(pka):
@@ -99,7 +115,8 @@ def test_config5_mixed_step_full(pka, seed):
     pka.paged_attn_decode(ds.decode_q, ds.k_cache, ds.v_cache, ds.decode_block_tables, ds.decode_context_lens,
                           step.scale, int(step.decode_context_lens.max()), out=out[:nd])
     pka.paged_attn_prefill(ds.prefill_q, ds.k_cache, ds.v_cache, ds.prefill_block_tables, ds.prefill_context_lens,
-                           ds.query_start_loc, step.scale, step.max_query_len, out=out[nd:])
+                           ds.query_start_loc, step.scale, step.max_query_len, int(step.prefill_context_lens.max()),
+                           out=out[nd:])
     torch.cuda.synchronize()
     kc, vc = oracle.kv_cache_write(step.new_k, step.new_v, step.slot_mapping, step.k_cache, step.v_cache)
     assert torch.equal(ds.k_cache.cpu().view(torch.int16), kc.view(torch.int16))
