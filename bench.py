@@ -44,6 +44,30 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 ROTATE_BYTES = 1 << 30          # rotate pools until at least 1 GiB is cycled
 
+# HBM bytes per launch of each workload's dominant kernel, from rocprofv3
+# FETCH_SIZE (x 2.0, the factor a 1 GiB copy calibrates) + WRITE_SIZE runs
+# (profiles/traffic_fetch_write.md), valid only for the kernel source they were
+# taken on: (source file, sha256 prefix, bytes).
+RECORDED_TRAFFIC = {
+    "decode_step": ("decode.hip", "9c1bf97e7ff6dd8e", 1189270016),
+    "splitk": ("decode.hip", "9c1bf97e7ff6dd8e", 270959840),
+    "mixed": ("prefill.hip", "9063986f76519a45", 45858272),
+}
+
+
+def recorded_traffic(workload):
+    """Traffic of the dominant kernel if its source is unchanged since the
+    counters were taken, else None."""
+    import hashlib
+
+    if workload not in RECORDED_TRAFFIC:
+        return None
+    fname, digest, nbytes = RECORDED_TRAFFIC[workload]
+    path = os.path.join(ROOT, "paged_kv_attention_21_amd", "csrc", fname)
+    with open(path, "rb") as f:
+        now = hashlib.sha256(f.read()).hexdigest()[:16]
+    return nbytes if now == digest else None
+
 
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -154,14 +178,18 @@ def bench_decode_step(args, pka):
     variant = pka.decode_choose_variant(S, step.num_kv_heads, max_ctx)
     ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, max_ctx)), dtype=torch.uint8, device="cuda:0")
 
+    writes = [pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r], prepare=True) for r in range(P.R)]
+    decs = [pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out, workspace=ws,
+                                  prepare=True) for r in range(P.R)]
+
     def launch(i, ev):
         r = i % P.R
         if ev:
             ev[0].record()
-        pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r])
+        writes[r]()
         if ev:
             ev[1].record()
-        pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out, workspace=ws)
+        decs[r]()
         if ev:
             ev[2].record()
 
@@ -204,14 +232,18 @@ def bench_splitk(args, pka):
     max_ctx = step.max_context_len
     bufs = pka.splitk_buffers(S, Hq, D, max_ctx, "cuda:0")
 
+    parts = [pka.paged_attn_decode_splitk(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, *bufs, prepare=True)
+             for r in range(P.R)]
+    reduce = pka.paged_attn_splitk_reduce(*bufs, P.cl, P.out, prepare=True)
+
     def launch(i, ev):
         r = i % P.R
         if ev:
             ev[0].record()
-        pka.paged_attn_decode_splitk(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, *bufs)
+        parts[r]()
         if ev:
             ev[1].record()
-        pka.paged_attn_splitk_reduce(*bufs, P.cl, P.out)
+        reduce()
         if ev:
             ev[2].record()
 
@@ -258,17 +290,23 @@ def bench_mixed(args, pka):
     pws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq,
                                                          step.num_kv_heads, D, mcl)), dtype=torch.uint8, device="cuda:0")
 
+    writes = [pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r], prepare=True) for r in range(P.R)]
+    decs = [pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws,
+                                  prepare=True) for r in range(P.R)]
+    pres = [pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, mcl, out=op, workspace=pws,
+                                   prepare=True) for r in range(P.R)]
+
     def launch(i, ev):
         r = i % P.R
         if ev:
             ev[0].record()
-        pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r])
+        writes[r]()
         if ev:
             ev[1].record()
-        pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws)
+        decs[r]()
         if ev:
             ev[2].record()
-        pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, mcl, out=op, workspace=pws)
+        pres[r]()
         if ev:
             ev[3].record()
 
@@ -317,11 +355,14 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
         S, Hq, D = step.decode_q.shape
         ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, ctx)), dtype=torch.uint8, device="cuda:0")
 
+        decs = [pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, ctx, out=P.out, workspace=ws,
+                                      prepare=True) for r in range(P.R)]
+
         def launch(i, ev):
             r = i % P.R
             if ev:
                 ev[0].record()
-            pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, ctx, out=P.out, workspace=ws)
+            decs[r]()
             if ev:
                 ev[1].record()
 
@@ -451,6 +492,8 @@ def main():
         "data": "synthetic (seeded N(0,1) q/K/V, seeded block tables and lengths)",
     }
     out.update(res)
+    if isinstance(out.get("roofline"), dict):
+        out["roofline"]["traffic"] = recorded_traffic(args.workload)
     if not args.no_cpu_baseline and step is not None:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline_decode(step, write, args.cpu_seconds)

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     PARTITION_SIZE,
     CacheDesc,
     PkaError,
+    Prepared,
     cache_desc,
     decode_choose_variant,
     device_cu_count,

@@ -116,6 +116,29 @@ def _check(status: int):
         raise PkaError(status, lib.pka_status_str(status).decode())
 
 
+class Prepared:
+    """A library call whose arguments were checked and marshalled once.
+    Calling it launches the same kernels again on the stream captured at
+    preparation, with one ctypes call (what a serving loop or a timing loop
+    wants).  The tensors it refers to are kept alive with it."""
+
+    __slots__ = ("fn", "args", "keep", "result")
+
+    def __init__(self, fn, args, keep, result=None):
+        self.fn, self.args, self.keep, self.result = fn, args, keep, result
+
+    def __call__(self):
+        _check(self.fn(*self.args))
+        return self.result
+
+
+def _launch(fn, args, prepare, keep, result=None):
+    if prepare:
+        return Prepared(fn, tuple(args), keep, result)
+    _check(fn(*args))
+    return result
+
+
 def _ptr(t: torch.Tensor | None):
     return c_void_p(t.data_ptr()) if t is not None else c_void_p(0)
 
@@ -176,7 +199,7 @@ def device_cu_count() -> int:
     return n
 
 
-def kv_cache_write(key, value, slot_mapping, k_cache, v_cache) -> None:
+def kv_cache_write(key, value, slot_mapping, k_cache, v_cache, prepare=False):
     """Scatter key/value [T, Hkv, D] into the pool at slot_mapping (int64 [T];
     negative = skip).  Bit-exact byte copy."""
     _check_pool(k_cache, v_cache)
@@ -187,8 +210,9 @@ def kv_cache_write(key, value, slot_mapping, k_cache, v_cache) -> None:
     T = key.shape[0]
     if value.shape != key.shape or slot_mapping.shape[0] != T or key.shape[1:] != k_cache.shape[2:]:
         raise ValueError("key/value/slot_mapping shapes disagree with each other or the pool")
-    _check(lib.pka_kv_cache_write(_ptr(key), _ptr(value), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
-                                  cache_desc(k_cache), _stream(k_cache)))
+    return _launch(lib.pka_kv_cache_write,
+                   (_ptr(key), _ptr(value), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cache_desc(k_cache),
+                    _stream(k_cache)), prepare, (key, value, slot_mapping, k_cache, v_cache))
 
 
 def _decode_common(q, k_cache, v_cache, block_tables, context_lens):
@@ -209,15 +233,15 @@ def _out_like(q, out):
     return out
 
 
-def paged_attn_decode_v1(q, k_cache, v_cache, block_tables, context_lens, scale, out=None):
+def paged_attn_decode_v1(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, prepare=False):
     """Single-pass paged decode: q [S, Hq, D] -> out [S, Hq, D]."""
     _decode_common(q, k_cache, v_cache, block_tables, context_lens)
     out = _out_like(q, out)
     S, Hq, _ = q.shape
-    _check(lib.pka_paged_attn_decode_v1(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                        _ptr(context_lens), S, Hq, block_tables.shape[1], float(scale), _ptr(out),
-                                        cache_desc(k_cache), _stream(q)))
-    return out
+    return _launch(lib.pka_paged_attn_decode_v1,
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
+                    block_tables.shape[1], float(scale), _ptr(out), cache_desc(k_cache), _stream(q)),
+                   prepare, (q, k_cache, v_cache, block_tables, context_lens, out), out)
 
 
 def splitk_buffers(num_seqs, num_q_heads, head_dim, max_context_len, device):
@@ -230,7 +254,7 @@ def splitk_buffers(num_seqs, num_q_heads, head_dim, max_context_len, device):
 
 
 def paged_attn_decode_splitk(q, k_cache, v_cache, block_tables, context_lens, scale, tmp_out, max_logits, exp_sums,
-                             partition_size=PARTITION_SIZE):
+                             partition_size=PARTITION_SIZE, prepare=False):
     """Split-K partition pass; fills tmp_out [S, Hq, P, D], max_logits and
     exp_sums [S, Hq, P] (fp32) for every partition inside a context."""
     _decode_common(q, k_cache, v_cache, block_tables, context_lens)
@@ -242,13 +266,15 @@ def paged_attn_decode_splitk(q, k_cache, v_cache, block_tables, context_lens, sc
     P = tmp_out.shape[2]
     if tmp_out.shape != (S, Hq, P, D) or max_logits.shape != (S, Hq, P) or exp_sums.shape != (S, Hq, P):
         raise ValueError("split-K buffers have the wrong shape")
-    _check(lib.pka_paged_attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                            _ptr(context_lens), S, Hq, block_tables.shape[1], float(scale),
-                                            partition_size, P, _ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums),
-                                            cache_desc(k_cache), _stream(q)))
+    return _launch(lib.pka_paged_attn_decode_splitk,
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
+                    block_tables.shape[1], float(scale), partition_size, P, _ptr(tmp_out), _ptr(max_logits),
+                    _ptr(exp_sums), cache_desc(k_cache), _stream(q)),
+                   prepare, (q, k_cache, v_cache, block_tables, context_lens, tmp_out, max_logits, exp_sums))
 
 
-def paged_attn_splitk_reduce(tmp_out, max_logits, exp_sums, context_lens, out, partition_size=PARTITION_SIZE):
+def paged_attn_splitk_reduce(tmp_out, max_logits, exp_sums, context_lens, out, partition_size=PARTITION_SIZE,
+                             prepare=False):
     """Merge split-K partitions into out [S, Hq, D] (fp16 or bf16)."""
     dev = out.device
     _require(out, "out", ndim=3)
@@ -261,9 +287,10 @@ def paged_attn_splitk_reduce(tmp_out, max_logits, exp_sums, context_lens, out, p
         raise ValueError("reduce shapes disagree")
     if out.dtype not in _DTYPES:
         raise ValueError("out must be fp16 or bf16")
-    _check(lib.pka_paged_attn_splitk_reduce(_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _ptr(context_lens), S,
-                                            Hq, D, partition_size, P, _ptr(out), _DTYPES[out.dtype], _stream(out)))
-    return out
+    return _launch(lib.pka_paged_attn_splitk_reduce,
+                   (_ptr(tmp_out), _ptr(max_logits), _ptr(exp_sums), _ptr(context_lens), S, Hq, D, partition_size, P,
+                    _ptr(out), _DTYPES[out.dtype], _stream(out)),
+                   prepare, (tmp_out, max_logits, exp_sums, context_lens, out), out)
 
 
 def splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len) -> int:
@@ -277,7 +304,7 @@ def decode_choose_variant(num_seqs, num_kv_heads, max_context_len, num_cus=None)
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
-                      workspace=None):
+                      workspace=None, prepare=False):
     """Paged decode with the library's dispatcher (single pass or split-K +
     reduce).  max_context_len: host upper bound on context_lens.  workspace:
     optional uint8 device buffer of splitk_workspace_bytes(...) bytes; one is
@@ -292,10 +319,11 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ma
     if workspace is not None:
         _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
         ws_bytes = workspace.numel()
-    _check(lib.pka_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-                                     S, Hq, block_tables.shape[1], int(max_context_len), float(scale), _ptr(out),
-                                     cache_desc(k_cache), _ptr(workspace), ws_bytes, _stream(q)))
-    return out
+    return _launch(lib.pka_paged_attn_decode,
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
+                    block_tables.shape[1], int(max_context_len), float(scale), _ptr(out), cache_desc(k_cache),
+                    _ptr(workspace), ws_bytes, _stream(q)),
+                   prepare, (q, k_cache, v_cache, block_tables, context_lens, out, workspace), out)
 
 
 def prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
@@ -304,7 +332,7 @@ def prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, h
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, max_query_len,
-                       max_context_len, out=None, workspace=None):
+                       max_context_len, out=None, workspace=None, prepare=False):
     """Paged prefill over ragged chunks packed in q [Nq, Hq, D] (bottom-right
     causal; chunks attend to their cached prefix).  max_query_len /
     max_context_len: host upper bounds.  workspace: optional uint8 device
@@ -327,8 +355,8 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
     if workspace is not None:
         _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
         ws_bytes = workspace.numel()
-    _check(lib.pka_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-                                      _ptr(query_start_loc), S, Nq, int(max_query_len), int(max_context_len), Hq,
-                                      block_tables.shape[1], float(scale), _ptr(out), cache_desc(k_cache),
-                                      _ptr(workspace), ws_bytes, _stream(q)))
-    return out
+    return _launch(lib.pka_paged_attn_prefill,
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                    _ptr(query_start_loc), S, Nq, int(max_query_len), int(max_context_len), Hq, block_tables.shape[1],
+                    float(scale), _ptr(out), cache_desc(k_cache), _ptr(workspace), ws_bytes, _stream(q)),
+                   prepare, (q, k_cache, v_cache, block_tables, context_lens, query_start_loc, out, workspace), out)

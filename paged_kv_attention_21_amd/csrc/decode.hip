@@ -187,19 +187,18 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   };
 
   // Main loop, double-buffered over this wavefront's blocks: while a block is
-  // consumed the next one's 2*LPB loads are in flight.  Every issue is
-  // unconditional - near the end of a window the index is clamped, so a block
-  // may be fetched twice and the copy dropped - which keeps the number of
-  // loads in flight the same on every path, so each consume waits for its own
-  // loads only.  Table entries come 64 at a time (lane k holds the entry of
-  // the wave's block j0 + k).
+  // consumed the next one's 2*LPB loads are in flight.  The steady-state body
+  // issues unconditionally, so every consume in it waits for its own loads
+  // only; the 1-3 blocks left at the end of a window are peeled (their waits
+  // may be conservative, and no block is fetched twice).  Table entries come
+  // 64 at a time (lane k holds the entry of the wave's block j0 + k).
   uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
   for (int j0 = 0; j0 < nb_wave; j0 += kWave) {
     const int jn = min(kWave, nb_wave - j0);
     const int tbl_win = lane < jn ? tbl[wave + (j0 + lane) * W] : 0;
     const int blk_base = wave + j0 * W;  // range-relative index of the window's block 0
     issue(uniform_lane(tbl_win, 0), ka, va);
-    issue(uniform_lane(tbl_win, min(1, jn - 1)), kb2, vb2);
+    if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
     int j = 0;
     for (; j + 3 < jn; j += 2) {
       consume(ka, va, blk_base + j * W);
@@ -209,7 +208,7 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
     consume(ka, va, blk_base + j * W);
-    issue(uniform_lane(tbl_win, min(j + 2, jn - 1)), ka, va);
+    if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
     if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * W);
     if (rem == 3) consume(ka, va, blk_base + (j + 2) * W);
   }
@@ -365,7 +364,11 @@ splitk_reduce_kernel(const float* __restrict__ tmp_out, const float* __restrict_
 #ifndef PKA_DECODE_WAVES
 #define PKA_DECODE_WAVES 4
 #endif
-constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per decode workgroup
+constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per single-pass decode workgroup
+#ifndef PKA_SPLIT_WAVES
+#define PKA_SPLIT_WAVES 4
+#endif
+constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partition workgroup
 
 template <typename T, int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t stream) {
@@ -377,7 +380,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t s
                        a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0);
   } else {
     dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, true>), grid, dim3(kDecodeWaves * kWave), 0,
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true>), grid, dim3(kSplitWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, nullptr, a.tmp_out, a.max_logits, a.exp_sums,
                        a.max_num_partitions);
