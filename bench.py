@@ -80,6 +80,7 @@ def parse_args():
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP-graph replay)")
     return p.parse_args()
 
 
@@ -138,6 +139,26 @@ def timed_loop(launch, n_phases, steps, warmup):
     return wall_ms, phases
 
 
+def graph_step_ms(capture_fns, steps, warmup):
+    """Capture each step variant (one per pool copy) into a HIP graph via
+    torch.cuda.graph and time `steps` replays, cycling the variants.  Returns
+    the wall milliseconds per step."""
+    graphs = []
+    for fn in capture_fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def cpu_baseline_decode(step, write, budget_s):
     """Time the oracle (as is) on the step's inputs: KV write + decode of
     all sequences, repeated while the budget lasts (at least once)."""
@@ -194,6 +215,17 @@ def bench_decode_step(args, pka):
             ev[2].record()
 
     wall_ms, (write_ms, dec_ms) = timed_loop(launch, 2, args.steps, args.warmup)
+    eager_ms = wall_ms
+    graph_ms = None
+    if not args.no_graph:
+        # The same step launched as a captured HIP graph (how a serving loop
+        # replays its decode step); the captured calls read torch's capture stream.
+        def step_fn(r):
+            return lambda: (pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r]),
+                            pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out,
+                                                  workspace=ws))
+        graph_ms = graph_step_ms([step_fn(r) for r in range(P.R)], args.steps, args.warmup)
+        wall_ms = graph_ms
     dbytes = W.decode_bytes(step)
     wbytes = W.kv_write_bytes(step)
     value = (dbytes + wbytes) / (wall_ms * 1e-3) / 1e9
@@ -203,6 +235,8 @@ def bench_decode_step(args, pka):
         "value": round(value, 2),
         "unit": "GB/s",
         "ms_per_step": round(wall_ms, 4),
+        "step_launch": "hip-graph replay" if graph_ms is not None else "eager",
+        "eager_ms_per_step": round(eager_ms, 4),
         "decode_us_per_call": round(dec_ms * 1e3, 2),
         "kv_write_us_per_call": round(write_ms * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
