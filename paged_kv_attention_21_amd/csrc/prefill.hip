@@ -151,7 +151,12 @@ struct PfTile {
 
 __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
                                         int num_seqs, int bq, int tile, PfTile* t) {
-  if (!find_tile(qsl, num_seqs, bq, tile, &t->seq, &t->qt)) return false;
+  int seq, qt;
+  if (!find_tile(qsl, num_seqs, bq, tile, &seq, &qt)) return false;
+  // Uniform across the wavefront: keep it (and all that follows) in scalar
+  // registers so the loops and branches below are scalar-controlled.
+  t->seq = __builtin_amdgcn_readfirstlane(seq);
+  t->qt = __builtin_amdgcn_readfirstlane(qt);
   t->qstart = qsl[t->seq];
   t->qlen = qsl[t->seq + 1] - t->qstart;
   t->cached = context_lens[t->seq] - t->qlen;

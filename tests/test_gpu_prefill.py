@@ -78,6 +78,28 @@ def test_long_context_splits(pka, shape):
     assert_parity(out, oracle_prefill(step), dtype, f"long-context splits {shape}")
 
 
+def test_workspace_reuse_across_calls(pka):
+    """One workspace serves consecutive calls (same bits every time)."""
+    step = W.make_prefill_step(query_lens=[200, 64, 1], cached_lens=[3000, 1500, 5000], dtype=torch.bfloat16,
+                               num_q_heads=16, num_kv_heads=8, head_dim=128, seed=37, poison=True, write_new=False)
+    ds = DevStep(step)
+    mcl = int(step.prefill_context_lens.max())
+    need = pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, 16, 8, 128, mcl)
+    assert need > 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage-filled: contents are scratch
+    ref = oracle_prefill(step)
+    outs = []
+    for call in range(3):
+        say(f"prefill with a reused workspace, call {call}")
+        out = pka.paged_attn_prefill(ds.prefill_q, ds.k_cache, ds.v_cache, ds.prefill_block_tables,
+                                     ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len, mcl,
+                                     workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, ref, step.dtype, f"reused workspace call {call}")
+        outs.append(out.cpu().view(torch.int16))
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_shared_prefix_chunks(pka):
     """Chunks whose tables share one 256-token prefix (refcounted blocks),
     each starting right after the prefix or later."""
