@@ -204,6 +204,8 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
  * pka_prefill_workspace_bytes(...) bytes, 256-byte aligned; contents need no
  * initialisation and are scratch after the call).  When that size is 0 the
  * workspace may be NULL.  PKA_ERR_WORKSPACE if it is needed and too small.
+ * scale must be positive and finite (PKA_ERR_UNSUPPORTED otherwise): the
+ * kernel tracks each row's running maximum of the unscaled scores.
  */
 int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_tables, const int32_t* context_lens,

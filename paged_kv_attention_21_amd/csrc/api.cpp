@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 
 #include "launch.h"
@@ -285,6 +286,7 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   if (max_blocks_per_seq <= 0 || max_query_len == 0 || max_query_len > num_q_tokens) return PKA_ERR_SHAPE;
   if (max_context_len < max_query_len) return PKA_ERR_SHAPE;
   if (!pka::prefill_supported(cache.dtype == PKA_BF16, cache.head_dim, group)) return PKA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PKA_ERR_UNSUPPORTED;  // the running max assumes scale > 0
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKA_ERR_ALIGN;
   const size_t need = pka_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, cache.num_kv_heads,
                                                   cache.head_dim, max_context_len);

@@ -18,6 +18,7 @@ struct BF16 {};
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Elem;
@@ -38,6 +39,10 @@ struct Elem<F16> {
   static __device__ __forceinline__ uint16_t from_float(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
   }
+  // two at once, round to nearest even (one v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, half2_t));
+  }
 };
 
 // bf16: the upper half of an fp32.  dot2 is v_dot2c_f32_bf16.
@@ -52,6 +57,10 @@ struct Elem<BF16> {
   // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
   static __device__ __forceinline__ uint16_t from_float(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+  // two at once, round to nearest even (one v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf162_t));
   }
 };
 
@@ -106,15 +115,27 @@ __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
 __device__ __forceinline__ void permlane32_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// v_max_f32 without the NaN-quieting copies fmaxf adds for operands the
+// compiler cannot see into (the permlane results).
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float xor16_max(float x) {
   float a = x, b = x;
   permlane16_swap(a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float xor32_max(float x) {
   float a = x, b = x;
   permlane32_swap(a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float xor16_sum(float x) {
   float a = x, b = x;

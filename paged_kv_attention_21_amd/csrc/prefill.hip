@@ -63,9 +63,8 @@ struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return (uint32_t)Elem<BF16>::from_float(lo) | ((uint32_t)Elem<BF16>::from_float(hi) << 16);
-  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return Elem<BF16>::pack2(lo, hi); }
+  static constexpr uint32_t kOne2 = 0x3F803F80u;  // (1.0, 1.0)
 };
 
 template <>
@@ -74,9 +73,8 @@ struct Mfma<F16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8_t, a), __builtin_bit_cast(halfx8_t, b),
                                                   c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return (uint32_t)Elem<F16>::from_float(lo) | ((uint32_t)Elem<F16>::from_float(hi) << 16);
-  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return Elem<F16>::pack2(lo, hi); }
+  static constexpr uint32_t kOne2 = 0x3C003C00u;  // (1.0, 1.0)
 };
 
 constexpr int kPfWaves = 4;
@@ -88,12 +86,22 @@ constexpr int kPfBlock = 16;          // KV block size
 constexpr int kPfSplitBlocks = kPfSplitKeys / kPfBlock;
 constexpr float kPfSlack = 8.f;       // log2 growth of a row max tolerated before rescaling
 
+// LDS tiles.  Every row (of Q, K or V) takes 288 bytes whatever the head
+// size, and in K and V tiles the 16-byte pieces of rows 8..15 (mod 16) sit at
+// piece index XOR 8.  Measured on gfx950 (bank-conflict counters of single
+// wavefronts), this is the layout where the three read patterns of the kernel
+// - K rows as the MFMA A operand, Q rows as the B operand, and the
+// transposing V reads - all run without bank conflicts; unpadded or
+// 16-byte-padded rows cost two to four extra cycles per read.
 template <int D>
 struct PfLds {
-  static constexpr int ROW = D + 8;          // K and V tile row stride (elements), 16-byte aligned rows
+  static_assert(D == 64 || D == 128, "pieces 0..15 after the swizzle");
+  static constexpr int ROW = 144;             // row stride in elements (288 bytes)
   static constexpr int TILE = kPfKeys * ROW;  // one [32 keys][D] tile
   static constexpr int STAGE = 2 * TILE;      // K tile, then V tile
 };
+// Piece swizzle of K/V row `row`: 8 when bit 3 of the row is set.
+__device__ __forceinline__ int pf_swz(int row) { return (row & 8); }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
 // output lane i gets element i % 4 of the 8-byte pieces read by input lanes
@@ -167,13 +175,16 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
 }
 
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(kPfThreads)
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t max_splits,
                      float scale_log2, uint16_t* __restrict__ out, float* __restrict__ partial) {
   using MM = Mfma<T>;
+  using EL = Elem<T>;
+  constexpr uint32_t kOnes2 = MM::kOne2;
+  const float slack_raw = kPfSlack / scale_log2;  // kPfSlack in raw score units
   using LD = PfLds<D>;
   constexpr int BQ = kPfRows / G;     // query positions per tile
   constexpr int KSTEPS = D / 32;      // MFMA k-steps of QK^T
@@ -181,6 +192,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int NT = kPfRowsPerWave / 16;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kPfRows * LD::ROW];  // the tile's 128 q-rows
   __shared__ int s_tbl[kPfSplitBlocks];
 
   const int kvh = blockIdx.x;
@@ -208,24 +220,35 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (b < kPfSplitBlocks && lb * kPfBlock < ctx) s_tbl[b] = block_tables[(size_t)tl.seq * max_blocks_per_seq + lb];
   }
 
-  // Q^T fragments (B operand): q-row n of this lane in tile nt, dims 32s + 8blk .. +7.
-  uint4 qf[NT][KSTEPS];
+  // The tile's q-rows go to LDS once (row n = position n / G, head n % G of
+  // the group; rows past the chunk are zero); the Q^T B-operand fragments are
+  // read from there every key tile, which keeps 32 registers free for a
+  // second prefetch set.
   int pos_of[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = wave * kPfRowsPerWave + nt * 16 + l16;
-    const int pos = tl.q0 + n / G;
-    const int g = n % G;
+    const int pos = tl.q0 + (wave * kPfRowsPerWave + nt * 16 + l16) / G;
     pos_of[nt] = pos < tl.qlen ? pos : -1;
-    const uint16_t* qp = q + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + g) * D + 8 * blk;
+  }
+  constexpr int QPER = kPfRows * D / 8 / kPfThreads;  // 16-byte pieces of Q per thread
+  {
+    uint4 qv[QPER];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos < tl.qlen) v = *reinterpret_cast<const uint4*>(qp + 32 * s);
-      qf[nt][s] = v;
+    for (int r = 0; r < QPER; ++r) {  // all loads first, then all LDS writes
+      const int c = threadIdx.x + r * kPfThreads;
+      const int n = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int pos = tl.q0 + n / G;
+      qv[r] = make_uint4(0, 0, 0, 0);
+      if (pos < tl.qlen)
+        qv[r] = *reinterpret_cast<const uint4*>(q + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + col);
+    }
+#pragma unroll
+    for (int r = 0; r < QPER; ++r) {
+      const int c = threadIdx.x + r * kPfThreads;
+      *reinterpret_cast<uint4*>(q_lds + (c / (D / 8)) * LD::ROW + (c % (D / 8)) * 8) = qv[r];
     }
   }
-  __syncthreads();  // s_tbl
+  __syncthreads();  // s_tbl, q_lds
 
   // ---- global -> register -> LDS staging of one key tile ----
   // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (256 / (D/8)),
@@ -237,7 +260,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int PER = CHUNKS / kPfThreads;
   static_assert(CHUNKS % kPfThreads == 0, "whole passes over the tile");
   constexpr int ROWS_PER_PASS = kPfThreads / (D / 8);
-  uint4 kreg[PER], vreg[PER];
+  uint4 kreg_a[PER], vreg_a[PER], kreg_b[PER], vreg_b[PER];  // two prefetch sets
   const int my_row = threadIdx.x / (D / 8);           // row of pass 0
   const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
   const uint32_t goff = (uint32_t)((my_row % kPfBlock) * row_elems + (size_t)kvh * D + my_col);  // elements
@@ -246,17 +269,19 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // rows are fetched from memory the sequence owns and then zeroed.
   const int last_blk = (ctx - 1) / kPfBlock - k_lo / kPfBlock;  // last s_tbl entry inside the context
 
-  auto fetch = [&](int tile) {
+  auto fetch = [&](int tile, uint4 (&kreg)[PER], uint4 (&vreg)[PER]) {
     const int k0 = k_lo + tile * kPfKeys;
     const int b0 = (k0 - k_lo) / kPfBlock;
     const int pb0 = __builtin_amdgcn_readfirstlane(s_tbl[b0]);
     const int pb1 = __builtin_amdgcn_readfirstlane(s_tbl[min(b0 + 1, last_blk)]);
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int blk_of = (my_row + r * ROWS_PER_PASS) / kPfBlock;  // 0 or 1, wavefront-uniform
-      const size_t pb = blk_of == 0 ? (size_t)pb0 : (size_t)pb1;
-      kreg[r] = *reinterpret_cast<const uint4*>(k_cache + pb * blk_elems + goff);
-      vreg[r] = *reinterpret_cast<const uint4*>(v_cache + pb * blk_elems + goff);
+      // KV block of this pass: 0 or 1, the same for the whole wavefront, so the
+      // block's base address is scalar and each lane adds its 32-bit offset.
+      const int blk_of = __builtin_amdgcn_readfirstlane((my_row + r * ROWS_PER_PASS) / kPfBlock);
+      const size_t base = (size_t)(blk_of == 0 ? pb0 : pb1) * blk_elems;
+      kreg[r] = *reinterpret_cast<const uint4*>(k_cache + base + goff);
+      vreg[r] = *reinterpret_cast<const uint4*>(v_cache + base + goff);
     }
     if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
@@ -269,12 +294,13 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, const uint4 (&kreg)[PER], const uint4 (&vreg)[PER]) {
     uint16_t* ks = lds + buf * LD::STAGE;
     uint16_t* vs = ks + LD::TILE;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int off = (my_row + r * ROWS_PER_PASS) * LD::ROW + my_col;
+      const int row = my_row + r * ROWS_PER_PASS;
+      const int off = row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3);
       *reinterpret_cast<uint4*>(ks + off) = kreg[r];
       *reinterpret_cast<uint4*>(vs + off) = vreg[r];
     }
@@ -290,88 +316,128 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K row read by this lane in key half kt: key 8*(l16/4) + 4*kt + l16%4 of the tile.
+  // K row read by this lane in key half kt: key 8*(l16/4) + 4*kt + l16%4 of the
+  // tile; its pieces 4s + blk (< 8 for s < 2, >= 8 after) are swizzled by ksw.
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
+  const int ksw = pf_swz(krow0);  // 0 or 8, the same for both key halves
 
-  if (ntiles > 0) fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    stage(buf);
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
+  // Tile t is staged from register set t % 2; right after the barrier the same
+  // set starts fetching tile t + 2, so every fetch has two tiles of compute to
+  // land.  The issue is unconditional (the index is clamped at the end, so the
+  // last tile may be fetched again and dropped), which keeps the loads in
+  // flight the same on every path and each stage's wait exact.
+  auto compute = [&](int tile, int buf) {
     const uint16_t* ks = lds + buf * LD::STAGE;
     const uint16_t* vs = ks + LD::TILE;
     const int k0 = k_lo + tile * kPfKeys;
 
-    // S^T = K Q^T for both key halves and both q-row tiles.
+    // S^T = K Q^T for both key halves and both q-row tiles; the Q^T fragments
+    // come from LDS one k-step at a time.
     floatx4_t sacc[NT][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int nt = 0; nt < NT; ++nt) sacc[nt][0] = sacc[nt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KSTEPS; ++s) {
+      uint4 qb[NT];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + (krow0 + 4 * kt) * LD::ROW + 32 * s + 8 * blk);
+      for (int nt = 0; nt < NT; ++nt)
+        qb[nt] = *reinterpret_cast<const uint4*>(q_lds + (wave * kPfRowsPerWave + nt * 16 + l16) * LD::ROW +
+                                                 32 * s + 8 * blk);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = MM::mma(a, qf[nt][s], sacc[nt][kt]);
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + (krow0 + 4 * kt) * LD::ROW +
+                                                        8 * ((4 * s + blk) ^ ksw));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = MM::mma(a, qb[nt], sacc[nt][kt]);
       }
     }
 
-    // Online softmax per q-row; this lane holds keys 8*blk + 4*kt + i.
-    const bool diag = k0 + kPfKeys - 1 > tl.cached + tl.q0;  // some key of the tile is past some row's limit
+    // Online softmax per q-row; this lane holds keys 8*blk + 4*kt + i.  The
+    // running max m is kept in raw score units (the scale is positive), so a
+    // weight is exp2(s * c - m * c) with c = scale * log2(e): one fma and one
+    // exp per score.  Keys past a row's causal limit are masked only on the
+    // tiles that reach the diagonal (a wavefront-uniform test).
+    const bool diag = k0 + kPfKeys - 1 > tl.cached + tl.q0;
+    if (diag) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int limit = pos_of[nt] >= 0 ? tl.cached + pos_of[nt] : -1;  // last visible key of this q-row
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 8 * blk + 4 * kt + i > limit) sacc[nt][kt][i] = -INFINITY;
+      }
+    }
     uint4 pf[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float sv[2][4];
-      float mx = kNegBig;
-      const int limit = pos_of[nt] >= 0 ? tl.cached + pos_of[nt] : -1;  // last visible key of this q-row
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[nt][kt][i] * scale_log2;
-          if (diag && (k0 + 8 * blk + 4 * kt + i > limit)) v = -INFINITY;
-          sv[kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+      const floatx4_t& s0 = sacc[nt][0];
+      const floatx4_t& s1 = sacc[nt][1];
+      float mx = vmax(vmax3(vmax3(vmax3(s0[0], s0[1], s0[2]), s0[3], s1[0]), s1[1], s1[2]), s1[3]);
       mx = xor32_max(xor16_max(mx));
       // Lazy rescale: the reference max only moves when some row's max grows
-      // by more than kPfSlack (log2 units), so the accumulators (kept in
-      // AGPRs) are rescaled on a handful of tiles instead of on every one;
-      // weights stay below 2^kPfSlack, harmless for fp32 sums and the
-      // bf16/fp16 rounding of P (relative).
-      if (__ballot(mx > m[nt] + kPfSlack)) {
+      // by more than kPfSlack in log2 units, so the accumulators are rescaled
+      // on a handful of tiles instead of on every one; weights stay below
+      // 2^kPfSlack, harmless for fp32 sums and for the (relative) bf16/fp16
+      // rounding of P.
+      if (__ballot(mx > m[nt] + slack_raw)) {
         const float mnew = fmaxf(m[nt], mx);
-        const float alpha = fast_exp2(m[nt] - mnew);
+        const float alpha = fast_exp2((m[nt] - mnew) * scale_log2);
         m[nt] = mnew;
         lpart[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] *= alpha;
       }
-      float ps = 0.f;
+      const float mc = -m[nt] * scale_log2;
       float p[2][4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kt][i] = fast_exp2(sv[kt][i] - m[nt]);
-          ps += p[kt][i];
-        }
-      lpart[nt] += ps;
+        for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(__builtin_fmaf(sacc[nt][kt][i], scale_log2, mc));
       pf[nt] = make_uint4(MM::pack2(p[0][0], p[0][1]), MM::pack2(p[0][2], p[0][3]), MM::pack2(p[1][0], p[1][1]),
                           MM::pack2(p[1][2], p[1][3]));
+      // Row sums of the rounded weights, the same values the PV product uses.
+      lpart[nt] = EL::dot2(pf[nt].x, kOnes2, lpart[nt]);
+      lpart[nt] = EL::dot2(pf[nt].y, kOnes2, lpart[nt]);
+      lpart[nt] = EL::dot2(pf[nt].z, kOnes2, lpart[nt]);
+      lpart[nt] = EL::dot2(pf[nt].w, kOnes2, lpart[nt]);
     }
 
     // O^T += V^T P^T; the V^T operand (dims 16 dt + l16, keys 8 blk .. +7) comes
     // from the row-major V tile through two transposing reads.
+    // Rows 8 blk + l16/4 (+4 for the upper half): swizzled when blk is odd,
+    // which moves dims 0..63 up by 64 elements and dims 64..127 down by 64.
+    const int vsw = (blk & 1) * 64;
     const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 4 * (l16 & 3);
+    const uint16_t* vlo = vrd + vsw;   // dim tiles 0..3
+    const uint16_t* vhi = vrd - vsw;   // dim tiles 4..7
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      const uint2 lo = lds_read_tr16(vrd + 16 * dt);
-      const uint2 hi = lds_read_tr16(vrd + 4 * LD::ROW + 16 * dt);
+      const uint16_t* vp = (dt < 4 ? vlo : vhi) + 16 * dt;
+      const uint2 lo = lds_read_tr16(vp);
+      const uint2 hi = lds_read_tr16(vp + 4 * LD::ROW);
       const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt][dt] = MM::mma(a, pf[nt], o[nt][dt]);
+    }
+  };
+
+  const int last_tile = ntiles - 1;
+  if (ntiles > 0) {
+    fetch(0, kreg_a, vreg_a);
+    fetch(min(1, last_tile), kreg_b, vreg_b);
+  }
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    stage(0, kreg_a, vreg_a);
+    __syncthreads();
+    fetch(min(tile + 2, last_tile), kreg_a, vreg_a);
+    compute(tile, 0);
+    if (tile + 1 < ntiles) {
+      stage(1, kreg_b, vreg_b);
+      __syncthreads();
+      fetch(min(tile + 3, last_tile), kreg_b, vreg_b);
+      compute(tile + 1, 1);
     }
   }
 
@@ -387,7 +453,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int dt = 0; dt < DTILES; ++dt)
         *reinterpret_cast<floatx4_t*>(slot + (size_t)n * D + 16 * dt + 4 * blk) = o[nt][dt];
       if (blk == 0) {
-        slot[(size_t)kPfRows * D + n] = m[nt];
+        slot[(size_t)kPfRows * D + n] = m[nt] * scale_log2;  // log2 units for the merge
         slot[(size_t)kPfRows * D + kPfRows + n] = lt;
       }
       continue;
@@ -406,45 +472,76 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 // Merge the splits of every query tile that has more than one: per q-row,
 // M = max_s m_s, w_s = exp2(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s.
-// Two threads per q-row, each owning half of its dims, so the weights are
-// computed twice per row and every O load is an independent 16-byte read.
+// One workgroup per (query tile, KV head, quarter of the tile's rows); eight
+// threads per q-row, each owning D/8 consecutive dims, so every partial row is
+// read as whole 16-byte pieces, and the split loop is unrolled so several
+// splits' loads are in flight at once.
+constexpr int kMgRows = kPfRows / 4;        // q-rows per merge workgroup
+constexpr int kMgThreadsPerRow = kPfThreads / kMgRows;
+
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kPfThreads)
 paged_prefill_merge_kernel(const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
                            int32_t num_seqs, int32_t num_kv_heads, int32_t max_splits,
                            const float* __restrict__ partial, uint16_t* __restrict__ out) {
-  static_assert(kPfThreads == 2 * kPfRows, "two threads per q-row");
   constexpr int BQ = kPfRows / G;
-  constexpr int HALF = D / 2;
+  constexpr int DPT = D / kMgThreadsPerRow;  // dims per thread
+  constexpr int F4 = DPT / 4;
+  constexpr int UNROLL = 4;
+  static_assert(DPT % 8 == 0, "whole 16-byte output pieces");
   const int kvh = blockIdx.x;
   PfTile tl;
   if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, blockIdx.y, &tl)) return;
   if (tl.nsplit <= 1 || tl.nsplit > max_splits) return;
-  const int n = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
+  const int n = blockIdx.z * kMgRows + threadIdx.x / kMgThreadsPerRow;  // q-row in the tile
+  const int d0 = (threadIdx.x % kMgThreadsPerRow) * DPT;
   const int pos = tl.q0 + n / G;
   if (pos >= tl.qlen) return;
   const int num_q_heads = num_kv_heads * G;
   const size_t slot_stride = (size_t)num_kv_heads * pf_slot_floats(D);
   const float* base = partial + ((size_t)blockIdx.y * max_splits * num_kv_heads + kvh) * pf_slot_floats(D);
+  const float* mrow = base + (size_t)kPfRows * D + n;  // m of split s at mrow[s * slot_stride]
+  const float* lrow = mrow + kPfRows;
+  const int ns = tl.nsplit;
+
   float mm = kNegBig;
-  for (int s = 0; s < tl.nsplit; ++s) mm = fmaxf(mm, base[s * slot_stride + (size_t)kPfRows * D + n]);
+  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, mrow[s * slot_stride]);
+
   float lt = 0.f;
-  floatx4_t acc[HALF / 4];
+  floatx4_t acc[F4];
 #pragma unroll
-  for (int c = 0; c < HALF / 4; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < tl.nsplit; ++s) {
-    const float* sl = base + s * slot_stride;
-    const float w = fast_exp2(sl[(size_t)kPfRows * D + n] - mm);
-    lt += w * sl[(size_t)kPfRows * D + kPfRows + n];
-    const floatx4_t* po = reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + half * HALF);
+  for (int c = 0; c < F4; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + UNROLL <= ns; s += UNROLL) {
+    floatx4_t o[UNROLL][F4];
+    float w[UNROLL], l[UNROLL];
 #pragma unroll
-    for (int c = 0; c < HALF / 4; ++c) acc[c] += w * po[c];
+    for (int u = 0; u < UNROLL; ++u) {
+      const float* sl = base + (size_t)(s + u) * slot_stride;
+      w[u] = mrow[(s + u) * slot_stride];
+      l[u] = lrow[(s + u) * slot_stride];
+#pragma unroll
+      for (int c = 0; c < F4; ++c) o[u][c] = *reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + d0 + 4 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const float wu = fast_exp2(w[u] - mm);
+      lt += wu * l[u];
+#pragma unroll
+      for (int c = 0; c < F4; ++c) acc[c] += wu * o[u][c];
+    }
+  }
+  for (; s < ns; ++s) {
+    const float* sl = base + (size_t)s * slot_stride;
+    const float wu = fast_exp2(mrow[s * slot_stride] - mm);
+    lt += wu * lrow[s * slot_stride];
+#pragma unroll
+    for (int c = 0; c < F4; ++c) acc[c] += wu * *reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + d0 + 4 * c);
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* op = out + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + half * HALF;
+  uint16_t* op = out + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + d0;
 #pragma unroll
-  for (int c = 0; c < HALF / 8; ++c) {
+  for (int c = 0; c < F4 / 2; ++c) {
     const floatx4_t a = acc[2 * c] * inv, b = acc[2 * c + 1] * inv;
     *reinterpret_cast<uint4*>(op + 8 * c) = make_uint4(Mfma<T>::pack2(a[0], a[1]), Mfma<T>::pack2(a[2], a[3]),
                                                        Mfma<T>::pack2(b[0], b[1]), Mfma<T>::pack2(b[2], b[3]));
@@ -474,7 +571,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                      a.num_kv_heads, splits, a.scale * kLog2e, a.out, a.workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
-  hipLaunchKernelGGL((paged_prefill_merge_kernel<T, D, G>), dim3(a.num_kv_heads, (unsigned)tiles), dim3(kPfThreads),
+  hipLaunchKernelGGL((paged_prefill_merge_kernel<T, D, G>), dim3(a.num_kv_heads, (unsigned)tiles, kPfRows / kMgRows),
+                     dim3(kPfThreads),
                      0, stream, a.context_lens, a.query_start_loc, a.num_seqs, a.num_kv_heads, splits, a.workspace,
                      a.out);
   return hipGetLastError();

@@ -106,6 +106,8 @@ def test_prefill_validation(pka):
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 12, 8, 0.1, A, d, None, 0, None) == 2   # 12 % 8
     bad = _desc(pka, bs=32, hkv=8, d=128, dt=1)
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, bad, None, 0, None) == 3
+    for scale in (0.0, -0.1, float("inf"), float("nan")):  # the running max assumes a positive scale
+        assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, scale, A, d, None, 0, None) == 3
     # a tile can see more keys than one split holds: the workspace is required
     assert pf(A, A, A, A, A, A, 2, 10, 5, 5000, 16, 8, 0.1, A, d, None, 0, None) == 5
     need = pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 5000)
