@@ -77,13 +77,21 @@ struct Mfma<F16> {
   static constexpr uint32_t kOne2 = 0x3C003C00u;  // (1.0, 1.0)
 };
 
-constexpr int kPfWaves = 4;
+#ifndef PKA_PREFILL_WAVES
+#define PKA_PREFILL_WAVES 4
+#endif
+// Each wavefront owns 32 q-rows; all wavefronts of a workgroup share every
+// staged K/V tile, so more wavefronts per tile means fewer K/V bytes pulled
+// through L2 per MFMA flop (the kernel is bound by that traffic at 4 waves).
+constexpr int kPfWaves = PKA_PREFILL_WAVES;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 128;          // q-rows per query tile (positions x group heads)
 constexpr int kPfRowsPerWave = 32;    // two 16-row MFMA tiles
+constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // q-rows per query tile (positions x group heads)
 constexpr int kPfKeys = 32;           // keys per staged tile (two KV blocks)
 constexpr int kPfBlock = 16;          // KV block size
-constexpr int kPfSplitBlocks = kPfSplitKeys / kPfBlock;
+// Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
+// swizzle, no stride).  Loads use offsets well inside num_records.
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kPfSlack = 8.f;       // log2 growth of a row max tolerated before rescaling
 
 // LDS tiles.  Every row (of Q, K or V) takes 288 bytes whatever the head
@@ -192,8 +200,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int NT = kPfRowsPerWave / 16;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kPfRows * LD::ROW];  // the tile's 128 q-rows
-  __shared__ int s_tbl[kPfSplitBlocks];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kPfRows * LD::ROW];  // the tile's q-rows
 
   const int kvh = blockIdx.x;
   const int split = blockIdx.z;
@@ -212,13 +219,6 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int k_hi = min(tl.kend, k_lo + kPfSplitKeys);
   const int ntiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
   const size_t row_elems = (size_t)num_kv_heads * D;
-
-  // Block-table entries of this split (only entries inside the context are read).
-  {
-    const int b = threadIdx.x;
-    const int lb = k_lo / kPfBlock + b;
-    if (b < kPfSplitBlocks && lb * kPfBlock < ctx) s_tbl[b] = block_tables[(size_t)tl.seq * max_blocks_per_seq + lb];
-  }
 
   // The tile's q-rows go to LDS once (row n = position n / G, head n % G of
   // the group; rows past the chunk are zero); the Q^T B-operand fragments are
@@ -248,7 +248,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       *reinterpret_cast<uint4*>(q_lds + (c / (D / 8)) * LD::ROW + (c % (D / 8)) * 8) = qv[r];
     }
   }
-  __syncthreads();  // s_tbl, q_lds
+  __syncthreads();  // q_lds
 
   // ---- global -> register -> LDS staging of one key tile ----
   // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (256 / (D/8)),
@@ -257,52 +257,57 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // so its base address sits in scalar registers and each load adds a
   // per-lane 32-bit offset.
   constexpr int CHUNKS = kPfKeys * D / 8;             // 16-byte pieces per tile
-  constexpr int PER = CHUNKS / kPfThreads;
-  static_assert(CHUNKS % kPfThreads == 0, "whole passes over the tile");
+  // With more threads than pieces (head size 64 at 8 wavefronts) the upper
+  // threads move nothing.
+  constexpr int PER = CHUNKS >= kPfThreads ? CHUNKS / kPfThreads : 1;
+  static_assert(CHUNKS % kPfThreads == 0 || kPfThreads % CHUNKS == 0, "whole passes over the tile");
   constexpr int ROWS_PER_PASS = kPfThreads / (D / 8);
-  uint4 kreg_a[PER], vreg_a[PER], kreg_b[PER], vreg_b[PER];  // two prefetch sets
+  const bool mover = CHUNKS >= kPfThreads || (int)threadIdx.x < CHUNKS;
+  uint4 kreg_a[PER], kreg_b[PER], vreg_a[PER], vreg_b[PER];  // two prefetch sets per tensor
   const int my_row = threadIdx.x / (D / 8);           // row of pass 0
   const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
   const uint32_t goff = (uint32_t)((my_row % kPfBlock) * row_elems + (size_t)kvh * D + my_col);  // elements
   const size_t blk_elems = (size_t)kPfBlock * row_elems;
-  // A block past the context is replaced by the context's last block: its
-  // rows are fetched from memory the sequence owns and then zeroed.
-  const int last_blk = (ctx - 1) / kPfBlock - k_lo / kPfBlock;  // last s_tbl entry inside the context
+  // A block past the context is replaced by the context's last block (only
+  // table entries inside the context are read): its rows are fetched from
+  // memory the sequence owns and then zeroed.
 
-  auto fetch = [&](int tile, uint4 (&kreg)[PER], uint4 (&vreg)[PER]) {
+  // Rows of key tile `tile` of one cache (K or V) into registers.  The two
+  // physical blocks come from the block table through scalar loads; each
+  // block's base address goes into a buffer descriptor, so every lane's load
+  // is the descriptor plus its own constant byte offset and no per-lane
+  // address arithmetic is left in the loop.
+  const int32_t* __restrict__ tbl_row = block_tables + (size_t)tl.seq * max_blocks_per_seq;
+  const int lb_last = (ctx - 1) / kPfBlock;  // last logical block inside the context
+  const uint32_t goff_bytes = goff * 2u;
+  auto fetch = [&](const uint16_t* __restrict__ cache, int tile, uint4 (&reg)[PER]) {
+    if (!mover) return;  // whole wavefronts (rows past the tile)
     const int k0 = k_lo + tile * kPfKeys;
-    const int b0 = (k0 - k_lo) / kPfBlock;
-    const int pb0 = __builtin_amdgcn_readfirstlane(s_tbl[b0]);
-    const int pb1 = __builtin_amdgcn_readfirstlane(s_tbl[min(b0 + 1, last_blk)]);
+    const int lb0 = k0 / kPfBlock;
+    const int pb0 = tbl_row[lb0];
+    const int pb1 = tbl_row[min(lb0 + 1, lb_last)];
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      // KV block of this pass: 0 or 1, the same for the whole wavefront, so the
-      // block's base address is scalar and each lane adds its 32-bit offset.
+      // KV block of this pass: 0 or 1, the same for the whole wavefront.
       const int blk_of = __builtin_amdgcn_readfirstlane((my_row + r * ROWS_PER_PASS) / kPfBlock);
-      const size_t base = (size_t)(blk_of == 0 ? pb0 : pb1) * blk_elems;
-      kreg[r] = *reinterpret_cast<const uint4*>(k_cache + base + goff);
-      vreg[r] = *reinterpret_cast<const uint4*>(v_cache + base + goff);
+      const uint16_t* base = cache + (size_t)(blk_of == 0 ? pb0 : pb1) * blk_elems;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, 0x7fffffff, kBufferFlags);
+      reg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, goff_bytes, 0, 0));
     }
     if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) {
-          kreg[r] = make_uint4(0, 0, 0, 0);
-          vreg[r] = make_uint4(0, 0, 0, 0);
-        }
-      }
+      for (int r = 0; r < PER; ++r)
+        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) reg[r] = make_uint4(0, 0, 0, 0);
     }
   };
 
-  auto stage = [&](int buf, const uint4 (&kreg)[PER], const uint4 (&vreg)[PER]) {
-    uint16_t* ks = lds + buf * LD::STAGE;
-    uint16_t* vs = ks + LD::TILE;
+  auto stage = [&](uint16_t* dst, const uint4 (&reg)[PER]) {
+    if (!mover) return;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       const int row = my_row + r * ROWS_PER_PASS;
-      const int off = row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3);
-      *reinterpret_cast<uint4*>(ks + off) = kreg[r];
-      *reinterpret_cast<uint4*>(vs + off) = vreg[r];
+      *reinterpret_cast<uint4*>(dst + row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3)) = reg[r];
     }
   };
 
@@ -321,19 +326,9 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
   const int ksw = pf_swz(krow0);  // 0 or 8, the same for both key halves
 
-  // Tile t is staged from register set t % 2; right after the barrier the same
-  // set starts fetching tile t + 2, so every fetch has two tiles of compute to
-  // land.  The issue is unconditional (the index is clamped at the end, so the
-  // last tile may be fetched again and dropped), which keeps the loads in
-  // flight the same on every path and each stage's wait exact.
-  auto compute = [&](int tile, int buf) {
-    const uint16_t* ks = lds + buf * LD::STAGE;
-    const uint16_t* vs = ks + LD::TILE;
-    const int k0 = k_lo + tile * kPfKeys;
-
+  auto qk = [&](const uint16_t* ks, floatx4_t (&sacc)[NT][2]) {
     // S^T = K Q^T for both key halves and both q-row tiles; the Q^T fragments
     // come from LDS one k-step at a time.
-    floatx4_t sacc[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sacc[nt][0] = sacc[nt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -352,11 +347,21 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
 
-    // Online softmax per q-row; this lane holds keys 8*blk + 4*kt + i.  The
-    // running max m is kept in raw score units (the scale is positive), so a
-    // weight is exp2(s * c - m * c) with c = scale * log2(e): one fma and one
-    // exp per score.  Keys past a row's causal limit are masked only on the
-    // tiles that reach the diagonal (a wavefront-uniform test).
+  };
+
+  // Online softmax per q-row, in two parts; this lane holds keys 8*blk + 4*kt + i.
+  // The running max m is kept in raw score units (the scale is positive), so
+  // a weight is exp2(s * c - m * c) with c = scale * log2(e): one fma and one
+  // exp per score.
+  //
+  // Part 1: causal mask (only on tiles that reach the diagonal, a
+  // wavefront-uniform test), row max, and the lazy rescale: the reference max
+  // only moves when some row's max grows by more than kPfSlack in log2 units,
+  // so the accumulators are rescaled on a handful of tiles instead of on
+  // every one; weights stay below 2^kPfSlack, harmless for fp32 sums and for
+  // the (relative) bf16/fp16 rounding of P.
+  auto row_max = [&](int tile, floatx4_t (&sacc)[NT][2]) {
+    const int k0 = k_lo + tile * kPfKeys;
     const bool diag = k0 + kPfKeys - 1 > tl.cached + tl.q0;
     if (diag) {
 #pragma unroll
@@ -369,19 +374,16 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             if (k0 + 8 * blk + 4 * kt + i > limit) sacc[nt][kt][i] = -INFINITY;
       }
     }
-    uint4 pf[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const floatx4_t& s0 = sacc[nt][0];
       const floatx4_t& s1 = sacc[nt][1];
-      float mx = vmax(vmax3(vmax3(vmax3(s0[0], s0[1], s0[2]), s0[3], s1[0]), s1[1], s1[2]), s1[3]);
-      mx = xor32_max(xor16_max(mx));
-      // Lazy rescale: the reference max only moves when some row's max grows
-      // by more than kPfSlack in log2 units, so the accumulators are rescaled
-      // on a handful of tiles instead of on every one; weights stay below
-      // 2^kPfSlack, harmless for fp32 sums and for the (relative) bf16/fp16
-      // rounding of P.
-      if (__ballot(mx > m[nt] + slack_raw)) {
+      // This lane's max over its 8 keys; only when some lane exceeds the slack
+      // is the full row max (over the row's four lanes) formed and the row
+      // rescaled, so the common tile needs no cross-lane traffic.
+      const float lmx = vmax(vmax3(vmax3(vmax3(s0[0], s0[1], s0[2]), s0[3], s1[0]), s1[1], s1[2]), s1[3]);
+      if (__ballot(lmx > m[nt] + slack_raw)) {
+        const float mx = xor32_max(xor16_max(lmx));
         const float mnew = fmaxf(m[nt], mx);
         const float alpha = fast_exp2((m[nt] - mnew) * scale_log2);
         m[nt] = mnew;
@@ -389,6 +391,14 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
         for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] *= alpha;
       }
+    }
+  };
+
+  // Part 2, branch-free: weights, rounded to the input type, and their row sums
+  // (of the rounded values, the ones the PV product uses).
+  auto weights = [&](const floatx4_t (&sacc)[NT][2], uint4 (&pf)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       const float mc = -m[nt] * scale_log2;
       float p[2][4];
 #pragma unroll
@@ -397,13 +407,14 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(__builtin_fmaf(sacc[nt][kt][i], scale_log2, mc));
       pf[nt] = make_uint4(MM::pack2(p[0][0], p[0][1]), MM::pack2(p[0][2], p[0][3]), MM::pack2(p[1][0], p[1][1]),
                           MM::pack2(p[1][2], p[1][3]));
-      // Row sums of the rounded weights, the same values the PV product uses.
       lpart[nt] = EL::dot2(pf[nt].x, kOnes2, lpart[nt]);
       lpart[nt] = EL::dot2(pf[nt].y, kOnes2, lpart[nt]);
       lpart[nt] = EL::dot2(pf[nt].z, kOnes2, lpart[nt]);
       lpart[nt] = EL::dot2(pf[nt].w, kOnes2, lpart[nt]);
     }
+  };
 
+  auto pv = [&](const uint16_t* vs, const uint4 (&pf)[NT]) {
     // O^T += V^T P^T; the V^T operand (dims 16 dt + l16, keys 8 blk .. +7) comes
     // from the row-major V tile through two transposing reads.
     // Rows 8 blk + l16/4 (+4 for the upper half): swizzled when blk is odd,
@@ -423,22 +434,58 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
+  // Software pipeline over key tiles, one barrier per tile.  K and V tiles
+  // have two LDS buffers each; while tile t's softmax runs, the MFMAs of
+  // S(t+1) = K(t+1) Q^T are already issued, so the matrix pipe and the VALU
+  // work on different tiles at once.  Step t reads K(t+1) and V(t), then
+  // stages K(t+2) over K(t) and V(t+1) over V(t-1), and fetches K(t+4) and
+  // V(t+3) into the registers just written out: every global load has two
+  // steps to land.  Fetch indices are clamped at the last tile, so the issue
+  // count is the same on every path and each wait stays exact.
+  uint16_t* const kbuf0 = lds;
+  uint16_t* const kbuf1 = lds + LD::TILE;
+  uint16_t* const vbuf0 = lds + 2 * LD::TILE;
+  uint16_t* const vbuf1 = lds + 3 * LD::TILE;
+  floatx4_t s_a[NT][2], s_b[NT][2];
+  uint4 pf[NT];
   const int last_tile = ntiles - 1;
   if (ntiles > 0) {
-    fetch(0, kreg_a, vreg_a);
-    fetch(min(1, last_tile), kreg_b, vreg_b);
-  }
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    stage(0, kreg_a, vreg_a);
+    fetch(k_cache, 0, kreg_a);
+    fetch(v_cache, 0, vreg_a);
+    fetch(k_cache, min(1, last_tile), kreg_b);
+    stage(kbuf0, kreg_a);
+    stage(vbuf0, vreg_a);
+    stage(kbuf1, kreg_b);
+    fetch(k_cache, min(2, last_tile), kreg_a);
+    fetch(k_cache, min(3, last_tile), kreg_b);
+    fetch(v_cache, min(1, last_tile), vreg_b);
+    fetch(v_cache, min(2, last_tile), vreg_a);
     __syncthreads();
-    fetch(min(tile + 2, last_tile), kreg_a, vreg_a);
-    compute(tile, 0);
-    if (tile + 1 < ntiles) {
-      stage(1, kreg_b, vreg_b);
-      __syncthreads();
-      fetch(min(tile + 3, last_tile), kreg_b, vreg_b);
-      compute(tile + 1, 1);
-    }
+    qk(kbuf0, s_a);
+    row_max(0, s_a);
+    __syncthreads();  // K tile 0 is read by every wavefront before step 0 overwrites it
+  }
+  auto step = [&](int t, floatx4_t (&scur)[NT][2], floatx4_t (&snext)[NT][2], const uint16_t* kread,
+                  const uint16_t* vread, uint16_t* kdst, uint16_t* vdst, uint4 (&kst)[PER], uint4 (&vst)[PER]) {
+    // S(t+1) (issued unconditionally: past the last tile it reads a stale
+    // buffer and is never used) and the weights of tile t have no dependence
+    // on each other, so the compiler may interleave the MFMAs with the VALU
+    // and exp work.
+    qk(kread, snext);
+    weights(scur, pf);
+    pv(vread, pf);
+    // Row max of tile t+1 (and the rare rescale, after PV(t) has added tile t
+    // at the old scale).
+    if (t + 1 < ntiles) row_max(t + 1, snext);
+    stage(kdst, kst);
+    stage(vdst, vst);
+    fetch(k_cache, min(t + 4, last_tile), kst);
+    fetch(v_cache, min(t + 3, last_tile), vst);
+    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, s_a, s_b, kbuf1, vbuf0, kbuf0, vbuf1, kreg_a, vreg_b);
+    if (t + 1 < ntiles) step(t + 1, s_b, s_a, kbuf0, vbuf1, kbuf1, vbuf0, kreg_b, vreg_a);
   }
 
   // Lane holds dims 16*dt + 4*blk + i of q-row l16 of tile nt.
