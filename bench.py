@@ -51,7 +51,7 @@ ROTATE_BYTES = 1 << 30          # rotate pools until at least 1 GiB is cycled
 RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "9c1bf97e7ff6dd8e", 1189270016),
     "splitk": ("decode.hip", "9c1bf97e7ff6dd8e", 270959840),
-    "mixed": ("prefill.hip", "9063986f76519a45", 45858272),
+    "mixed": ("prefill.hip", "43dc6198ff6a4746", 45908160),
 }
 
 

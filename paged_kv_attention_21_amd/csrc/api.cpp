@@ -204,9 +204,11 @@ int32_t pka_decode_choose_variant(int32_t num_seqs, int32_t num_kv_heads, int32_
   if (max_context_len <= pka::kPartitionSize) return 1;
   if (num_cus <= 0) num_cus = 256;
   const int64_t units = (int64_t)num_seqs * num_kv_heads;
-  // Enough (sequence, KV head) workgroups to give every CU several, and no
-  // context so long that one workgroup's tail dominates: single pass.
-  if (units >= 4 * (int64_t)num_cus && max_context_len <= 4096) return 1;
+  // At least two (sequence, KV head) workgroups per CU, and no context so long
+  // that one workgroup's tail dominates: single pass.  (Measured on 256 CUs:
+  // 64 x 8 workgroups with contexts up to 2,048 run about as fast single-pass
+  // as split, without the partial-result traffic and the reduce launch.)
+  if (units >= 2 * (int64_t)num_cus && max_context_len <= 4096) return 1;
   return 2;
 }
 

@@ -124,3 +124,6 @@ def test_workspace_bytes_and_dispatcher(pka):
     assert cv(1, 2, 4096, 256) == 2           # single long request
     assert cv(4, 8, 16384, 256) == 2          # few sequences, long contexts
     assert cv(256, 8, 2048, 256) == 1         # 2048 (seq, head) workgroups on 256 CUs
+    assert cv(64, 8, 2048, 256) == 1          # mixed-step decodes: 512 workgroups, contexts <= 2048
+    assert cv(32, 8, 2048, 256) == 2          # 256 workgroups: one per CU, split instead
+    assert cv(64, 8, 8192, 256) == 2          # long contexts: split
