@@ -5,10 +5,14 @@ CPU-baseline leg of the benchmark, never by the GPU library, with which it
 shares no code.
 
 Parity pins (closed forms, invariants, library special cases and brute force
-that fix each function) live in tests/test_oracle_pins.py and
-tests/test_oracle_mutants.py.  Every function here is pinned; none is
+that fix each function) live in tests/test_oracle_pins.py,
+tests/test_oracle_mutants.py and tests/test_oracle_rope.py.  Every function here is pinned; none is
 "parity unpinned".
 """
 
+from . import rotary as _rotary
 from .paged_attention import *  # noqa: F401,F403
-from .paged_attention import __all__  # noqa: F401
+from .paged_attention import __all__ as _pa_all
+from .rotary import *  # noqa: F401,F403
+
+__all__ = list(_pa_all) + list(_rotary.__all__)
