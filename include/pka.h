@@ -111,6 +111,43 @@ int32_t pka_kv_cache_write(const void* key, const void* value, const int64_t* sl
                            pka_cache_desc cache, void* stream);
 
 /*
+ * Rotary table for pka_fused_rope_kv_write (mini_engine: "Roadmap", fused
+ * RoPE folded into the QKV split / KV-cache write).  Fills
+ *   table[p][i] = (cos a, sin a), a = p * theta^(-2 i / head_dim),
+ * for p < max_position, i < head_dim / 2, as fp32 pairs computed in double
+ * precision on the device.  table: device memory of
+ * pka_rope_table_bytes(max_position, head_dim) bytes, 16-byte aligned, owned
+ * by the caller; fill it once per (theta, head_dim).  theta must be > 1 and
+ * head_dim a multiple of 16 (PKA_ERR_SHAPE otherwise).
+ */
+int32_t pka_rope_table(float* table, int32_t max_position, int32_t head_dim, double theta, void* stream);
+size_t pka_rope_table_bytes(int32_t max_position, int32_t head_dim);
+
+/*
+ * Rotary embedding fused into the KV-cache write (mini_engine: "Roadmap";
+ * [MS] fused qkv projection, RoPE, then index_copy_ into the pool).  Reads
+ * each token's fused projection row
+ *   qkv[t] = [q heads (num_q_heads x head_dim) | k heads | v heads
+ *             (num_kv_heads x head_dim each)], element stride qkv_row_stride,
+ * rotates q and k by positions[t] with the rotate-half pairing (element
+ * i < D/2 pairs with i + D/2; the pair turns by the table's angle), writes the
+ * rotated q to q_out [num_tokens][num_q_heads][head_dim] (contiguous), and for
+ * slot_mapping[t] >= 0 stores the rotated k and the unchanged v bits at that
+ * slot of k_cache / v_cache.  Negative slots are padding: their q is still
+ * rotated, nothing is written to the pool.  Rotation in fp32, one rounding
+ * (to nearest even) to the cache type.
+ *   positions     int64 [num_tokens], 0 <= positions[t] < max_position
+ *                 (device precondition, unchecked)
+ *   rope_table    as filled by pka_rope_table for this head_dim
+ * PKA_ERR_SHAPE if qkv_row_stride is below the row length or breaks 16-byte
+ * alignment of the rows.
+ */
+int32_t pka_fused_rope_kv_write(const void* qkv, int64_t qkv_row_stride, const int64_t* positions,
+                                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                                const float* rope_table, int32_t max_position, void* q_out, void* k_cache,
+                                void* v_cache, pka_cache_desc cache, void* stream);
+
+/*
  * Paged decode, single pass ([MLR] CUDA PagedAttention; [ME] decode v1).
  * One query row per sequence; out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
  * over the first context_lens[s] tokens of sequence s, K_s and V_s read in

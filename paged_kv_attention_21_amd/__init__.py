@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     cache_desc,
     decode_choose_variant,
     device_cu_count,
+    fused_rope_kv_write,
     kv_cache_write,
     paged_attn_decode,
     paged_attn_decode_splitk,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     paged_attn_prefill,
     paged_attn_splitk_reduce,
     prefill_workspace_bytes,
+    rope_table,
     splitk_buffers,
     splitk_workspace_bytes,
     version,

@@ -86,6 +86,13 @@ _SIGNATURES = {
          c_int32, c_float, c_void_p, CacheDesc, c_void_p, c_size_t, c_void_p],
     ),
     "pka_prefill_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pka_rope_table": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
+    "pka_rope_table_bytes": (c_size_t, [c_int32, c_int32]),
+    "pka_fused_rope_kv_write": (
+        c_int32,
+        [c_void_p, ctypes.c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+         c_void_p, CacheDesc, c_void_p],
+    ),
 }
 
 
@@ -213,6 +220,47 @@ def kv_cache_write(key, value, slot_mapping, k_cache, v_cache, prepare=False):
     return _launch(lib.pka_kv_cache_write,
                    (_ptr(key), _ptr(value), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cache_desc(k_cache),
                     _stream(k_cache)), prepare, (key, value, slot_mapping, k_cache, v_cache))
+
+
+def rope_table(max_position, head_dim, theta, device):
+    """Device table of (cos, sin) fp32 pairs [max_position, head_dim / 2, 2]
+    for the fused RoPE write, computed on the GPU (double precision)."""
+    n = lib.pka_rope_table_bytes(int(max_position), int(head_dim)) // 4
+    table = torch.empty(max(n, 1), dtype=torch.float32, device=device)
+    with torch.cuda.device(table.device):
+        _check(lib.pka_rope_table(_ptr(table), int(max_position), int(head_dim), float(theta), _stream(table)))
+    return table[:n].view(int(max_position), int(head_dim) // 2, 2)
+
+
+def fused_rope_kv_write(qkv, positions, slot_mapping, table, num_q_heads, k_cache, v_cache, q_out=None,
+                        prepare=False):
+    """Rotate q and k of the fused projection rows qkv [T, (Hq + 2 Hkv) * D]
+    (row stride may exceed the row) by positions (int64 [T]); returns
+    q_out [T, Hq, D] and writes rotated k and raw v into the pool at
+    slot_mapping (int64 [T]; negative = padding)."""
+    _check_pool(k_cache, v_cache)
+    dev = k_cache.device
+    _require(qkv, "qkv", dtype=k_cache.dtype, ndim=2, device=dev)
+    _require(positions, "positions", dtype=torch.int64, ndim=1, device=dev)
+    _require(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1, device=dev)
+    _require(table, "table", dtype=torch.float32, ndim=3, device=dev)
+    T = qkv.shape[0]
+    Hkv, D = k_cache.shape[2], k_cache.shape[3]
+    if qkv.stride(1) != 1 or qkv.shape[1] != (num_q_heads + 2 * Hkv) * D:
+        raise ValueError("qkv rows must be [q heads | k heads | v heads] with unit element stride")
+    if positions.shape[0] != T or slot_mapping.shape[0] != T:
+        raise ValueError("positions/slot_mapping length differs from qkv rows")
+    if table.shape[1] * 2 != D or not table.is_contiguous():
+        raise ValueError("rope table does not match the head size")
+    if q_out is None:
+        q_out = torch.empty((T, num_q_heads, D), dtype=qkv.dtype, device=dev)
+    _require(q_out, "q_out", dtype=qkv.dtype, ndim=3, device=dev)
+    if q_out.shape != (T, num_q_heads, D) or not q_out.is_contiguous():
+        raise ValueError("q_out must be contiguous [T, Hq, D]")
+    return _launch(lib.pka_fused_rope_kv_write,
+                   (_ptr(qkv), qkv.stride(0), _ptr(positions), _ptr(slot_mapping), T, int(num_q_heads), _ptr(table),
+                    table.shape[0], _ptr(q_out), _ptr(k_cache), _ptr(v_cache), cache_desc(k_cache), _stream(k_cache)),
+                   prepare, (qkv, positions, slot_mapping, table, q_out, k_cache, v_cache), q_out)
 
 
 def _decode_common(q, k_cache, v_cache, block_tables, context_lens):

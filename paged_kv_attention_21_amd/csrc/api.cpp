@@ -126,6 +126,52 @@ int32_t pka_kv_cache_write(const void* key, const void* value, const int64_t* sl
   return hip_status(pka::launch_kv_write(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pka_rope_table(float* table, int32_t max_position, int32_t head_dim, double theta, void* stream) {
+  if (max_position < 0 || head_dim <= 0 || head_dim % 16) return PKA_ERR_SHAPE;
+  if (!(theta > 1.0) || !std::isfinite(theta)) return PKA_ERR_SHAPE;
+  if (max_position == 0) return PKA_OK;
+  if (!table) return PKA_ERR_NULL;
+  if (!aligned16(table)) return PKA_ERR_ALIGN;
+  return hip_status(pka::launch_rope_table(table, max_position, head_dim, theta, static_cast<hipStream_t>(stream)));
+}
+
+size_t pka_rope_table_bytes(int32_t max_position, int32_t head_dim) {
+  if (max_position <= 0 || head_dim <= 0) return 0;
+  return (size_t)max_position * (size_t)head_dim * sizeof(float);
+}
+
+int32_t pka_fused_rope_kv_write(const void* qkv, int64_t qkv_row_stride, const int64_t* positions,
+                                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_q_heads,
+                                const float* rope_table, int32_t max_position, void* q_out, void* k_cache,
+                                void* v_cache, pka_cache_desc cache, void* stream) {
+  if (num_tokens < 0 || max_position <= 0) return PKA_ERR_SHAPE;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (cache.head_dim % 16) return PKA_ERR_UNSUPPORTED;
+  if (num_q_heads <= 0) return PKA_ERR_SHAPE;
+  const int64_t row = (int64_t)(num_q_heads + 2 * cache.num_kv_heads) * cache.head_dim;
+  if (qkv_row_stride < row || (qkv_row_stride * elem_size(cache.dtype)) % 16) return PKA_ERR_SHAPE;
+  if (num_tokens == 0) return PKA_OK;
+  if (!qkv || !positions || !slot_mapping || !rope_table || !q_out || !k_cache || !v_cache) return PKA_ERR_NULL;
+  if (!aligned16(qkv) || !aligned16(rope_table) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKA_ERR_ALIGN;
+  pka::RopeKvArgs a{};
+  a.qkv = static_cast<const uint16_t*>(qkv);
+  a.row_stride = qkv_row_stride;
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.table = rope_table;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache.num_kv_heads;
+  a.head_dim = cache.head_dim;
+  a.bf16 = cache.dtype == PKA_BF16;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  return hip_status(pka::launch_rope_kv_write(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pka_paged_attn_decode_v1(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq, float scale, void* out,

@@ -83,7 +83,22 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream);
+struct RopeKvArgs {
+  const uint16_t* qkv;       // [T, row_stride] rows: q heads, k heads, v heads
+  int64_t row_stride;        // elements between consecutive token rows
+  const int64_t* positions;  // [T]
+  const int64_t* slot_mapping;
+  const float* table;        // [max_position][head_dim / 2] (cos, sin) pairs
+  int32_t num_tokens, num_q_heads, num_kv_heads, head_dim;
+  bool bf16;
+  uint16_t* q_out;           // [T, Hq, D]
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+};
+
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_rope_table(float* table, int max_position, int head_dim, double theta, hipStream_t stream);
+hipError_t launch_rope_kv_write(const RopeKvArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(bool bf16, int head_dim, int group);
 size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,

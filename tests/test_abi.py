@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for name in ("pka_kv_cache_write", "pka_paged_attn_decode", "pka_paged_attn_decode_v1",
                  "pka_paged_attn_decode_splitk", "pka_paged_attn_splitk_reduce", "pka_paged_attn_prefill",
                  "pka_splitk_workspace_bytes", "pka_decode_choose_variant", "pka_status_str",
-                 "pka_prefill_workspace_bytes"):
+                 "pka_prefill_workspace_bytes", "pka_rope_table", "pka_rope_table_bytes", "pka_fused_rope_kv_write"):
         assert name in syms
 
 
@@ -127,3 +127,23 @@ def test_workspace_bytes_and_dispatcher(pka):
     assert cv(64, 8, 2048, 256) == 1          # mixed-step decodes: 512 workgroups, contexts <= 2048
     assert cv(32, 8, 2048, 256) == 2          # 256 workgroups: one per CU, split instead
     assert cv(64, 8, 8192, 256) == 2          # long contexts: split
+
+
+def test_rope_validation(pka):
+    """Host-side checks of the RoPE entry points (nothing is launched)."""
+    lib = pka._lib.lib
+    d = _desc(pka, hkv=8, d=128, dt=1)
+    assert lib.pka_rope_table_bytes(4096, 128) == 4096 * 128 * 4
+    assert lib.pka_rope_table_bytes(0, 128) == 0
+    assert lib.pka_rope_table(A, 10, 100, 1e4, None) == 2       # head_dim not a multiple of 16
+    assert lib.pka_rope_table(A, 10, 128, 1.0, None) == 2       # theta must exceed 1
+    assert lib.pka_rope_table(None, 10, 128, 1e4, None) == 1
+    assert lib.pka_rope_table(A, 0, 128, 1e4, None) == 0        # nothing to fill
+    f = lib.pka_fused_rope_kv_write
+    row = (16 + 16) * 128
+    assert f(A, row, A, A, 0, 16, A, 4096, A, A, A, d, None) == 0          # no tokens
+    assert f(A, row - 8, A, A, 4, 16, A, 4096, A, A, A, d, None) == 2      # stride below the row
+    assert f(A, row + 4, A, A, 4, 16, A, 4096, A, A, A, d, None) == 2      # rows not 16-byte aligned
+    assert f(A, row, None, A, 4, 16, A, 4096, A, A, A, d, None) == 1
+    assert f(A, row, A, A, 4, 16, A, 0, A, A, A, d, None) == 2             # empty table
+    assert f(A, row, A, A, 4, 0, A, 4096, A, A, A, d, None) == 2           # no q heads

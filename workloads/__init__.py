@@ -16,6 +16,7 @@ from .synth import (  # noqa: F401
     config_3,
     config_4,
     config_5,
+    fused_qkv,
     CONFIG_NAMES,
 )
-from .accounting import decode_bytes, kv_write_bytes, prefill_bytes, prefill_flops  # noqa: F401
+from .accounting import decode_bytes, kv_write_bytes, prefill_bytes, prefill_flops, rope_kv_write_bytes  # noqa: F401

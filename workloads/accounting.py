@@ -8,6 +8,9 @@ kernel has to touch once:
   the block-table entries that cover the context, and the context lengths;
 * KV write: each non-skipped new K and V row read once and written once, plus
   the slot indices;
+* rotary KV write: the fused projection rows read once, rotated q written
+  once, each non-skipped k and v row written once, positions and slots, and
+  one table row (head_dim fp32) per distinct position;
 * prefill: 4 * head_dim * num_q_heads FLOPs per (query row, visible key) pair
   (QK^T and PV, 2 FLOPs per multiply-add), counting only keys the causal mask
   keeps: a chunk of q rows after c cached tokens sees q*c + q*(q+1)/2 pairs.
@@ -43,6 +46,17 @@ def kv_write_bytes(step) -> int:
     rows = int((step.slot_mapping >= 0).sum())
     row_bytes = step.num_kv_heads * step.head_dim * e
     return rows * row_bytes * 2 * 2 + 8 * int(step.slot_mapping.numel())
+
+
+def rope_kv_write_bytes(step) -> int:
+    """Minimum HBM bytes of one fused rotary + KV-cache write call."""
+    e = _elt(step.dtype)
+    T = int(step.slot_mapping.numel())
+    D, Hq, Hkv = step.head_dim, step.num_q_heads, step.num_kv_heads
+    rows = int((step.slot_mapping >= 0).sum())
+    read = T * (Hq + 2 * Hkv) * D * e + 16 * T + int(torch.unique(step.positions).numel()) * D * 4
+    write = T * Hq * D * e + rows * 2 * Hkv * D * e
+    return read + write
 
 
 def prefill_flops(step) -> int:

@@ -92,6 +92,8 @@ class PagedStep:
     refcount: np.ndarray
     poisoned: bool
     meta: dict = field(default_factory=dict)
+    # Position (logical token index) of every new row, in q-row order.
+    positions: torch.Tensor | None = None
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -337,6 +339,7 @@ def _build(
         new_k=new_k,
         new_v=new_v,
         slot_mapping=slot_mapping,
+        positions=torch.tensor([p for row in new_positions for p in row], dtype=torch.int64),
         sentinel_block=sentinel,
         refcount=refcount,
         poisoned=poison,
@@ -552,3 +555,13 @@ def config_5(seed=0, poison=False, budget=2048, num_decode=64, max_chunk=512,
         pool_factor=1.1, write_new=True, poison=poison, rng=rng, vgen=vgen,
         meta=dict(prompt_lens=prompt, budget=budget),
     )
+
+
+def fused_qkv(step: PagedStep) -> torch.Tensor:
+    """The step's new rows as the fused projection output the rotary write
+    consumes: [T, (Hq + 2 Hkv) * D] = [q heads | k heads | v heads] per row
+    (q from step.q, k and v from step.new_k / step.new_v)."""
+    if step.new_k is None:
+        raise ValueError("step has no new K/V rows (built with write_new=False)")
+    T = step.q.shape[0]
+    return torch.cat([step.q, step.new_k, step.new_v], dim=1).reshape(T, -1).contiguous()
