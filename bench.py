@@ -43,6 +43,7 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 ROTATE_BYTES = 1 << 30          # rotate pools until at least 1 GiB is cycled
+ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen3 checkpoints)
 
 # HBM bytes per launch of each workload's dominant kernel, from rocprofv3
 # FETCH_SIZE (x 2.0, the factor a 1 GiB copy calibrates) + WRITE_SIZE runs
@@ -51,6 +52,7 @@ ROTATE_BYTES = 1 << 30          # rotate pools until at least 1 GiB is cycled
 RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "9c1bf97e7ff6dd8e", 1189270016),
     "splitk": ("decode.hip", "9c1bf97e7ff6dd8e", 270959840),
+    "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
     "mixed": ("prefill.hip", "43dc6198ff6a4746", 45908160),
 }
 
@@ -75,7 +77,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_step",
-                   choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy"])
+                   choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
@@ -453,6 +455,101 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
     return res, step, False
 
 
+def cpu_baseline_rope(step, budget_s, rows=256):
+    """Time the oracle (as is) on the first `rows` new rows of the step."""
+    import oracle
+
+    qkv = W.fused_qkv(step)[:rows]
+    pos, slots = step.positions[:rows], step.slot_mapping[:rows]
+    threads = torch.get_num_threads()
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.fused_rope_kv_write(qkv, pos, slots, step.k_cache, step.v_cache, step.num_q_heads, step.num_kv_heads,
+                                   ROPE_THETA)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el * (passes + 1) / passes > 3 * budget_s:
+            break
+    per_pass = el / passes
+    e = step.q.element_size()
+    D, Hq, Hkv = step.head_dim, step.num_q_heads, step.num_kv_heads
+    nbytes = rows * ((Hq + 2 * Hkv) * D * e + 16 + D * 4 + Hq * D * e + 2 * Hkv * D * e)
+    return {
+        "value": round(nbytes / per_pass / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 torch-CPU oracle: fused rotary + KV write of the first {rows} of {step.q.shape[0]} rows "
+                  f"(the pool is cloned once per call), {passes} pass(es) in {el:.1f} s",
+        "ms_per_step": round(per_pass * 1e3, 2),
+    }
+
+
+def bench_rope(args, pka):
+    """Fused rotary + KV write of the mixed step's 2,048 new rows, next to the
+    eager arm it replaces (torch rotation of q and k, then the KV write)."""
+    step = W.config_5(seed=args.seed)
+    dev = torch.device("cuda:0")
+    T, Hq, D = step.q.shape
+    Hkv = step.num_kv_heads
+    max_pos = 8192
+    assert int(step.positions.max()) < max_pos
+    qkv = W.fused_qkv(step).to(dev)
+    pos = step.positions.to(dev)
+    slots = step.slot_mapping.to(dev)
+    kc, vc = step.k_cache.to(dev), step.v_cache.to(dev)
+    table = pka.rope_table(max_pos, D, ROPE_THETA, dev)
+    q_out = torch.empty((T, Hq, D), dtype=step.dtype, device=dev)
+    fused = pka.fused_rope_kv_write(qkv, pos, slots, table, Hq, kc, vc, q_out=q_out, prepare=True)
+
+    rows = qkv.view(T, Hq + 2 * Hkv, D)
+    cs = table[pos]  # [T, D/2, 2]
+    cos, sin = cs[..., 0].unsqueeze(1), cs[..., 1].unsqueeze(1)
+
+    def eager():
+        x = rows[:, :Hq + Hkv].float()
+        lo, hi = x[..., :D // 2], x[..., D // 2:]
+        rot = torch.cat([lo * cos - hi * sin, hi * cos + lo * sin], dim=-1).to(step.dtype)
+        q_out.copy_(rot[:, :Hq])
+        pka.kv_cache_write(rot[:, Hq:].contiguous(), rows[:, Hq + Hkv:].contiguous(), slots, kc, vc)
+
+    def launch(i, ev):
+        if ev:
+            ev[0].record()
+        fused()
+        if ev:
+            ev[1].record()
+        eager()
+        if ev:
+            ev[2].record()
+
+    wall_ms, (fused_ms, eager_ms) = timed_loop(launch, 2, args.steps, args.warmup)
+    nbytes = W.rope_kv_write_bytes(step)
+    gbps = nbytes / (fused_ms * 1e-3) / 1e9
+    res = {
+        "metric": "fused rotary + KV-cache write GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(fused_ms, 4),
+        "fused_us_per_call": round(fused_ms * 1e3, 2),
+        "eager_arm_us_per_call": round(eager_ms * 1e3, 2),
+        "dtype": "bf16",
+        "config": {
+            "workload": "fused rotary embedding + KV-cache write of the mixed step's 2048 new rows, bf16, 16q/8kv, "
+                        "head_dim 128, rotate-half RoPE, theta 1e6",
+            "rows": T, "max_position": max_pos, "seed": args.seed, "algorithmic_bytes": nbytes,
+            "eager_arm": "torch fp32 rotation of q and k + separate KV write (the pass the fusion removes)",
+        },
+        "roofline": {"kernel": "rope_kv_write_kernel", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline_rope(step, args.cpu_seconds)
+    return res, None, False
+
+
 def bench_copy(args):
     """Calibration: a plain device-to-device copy of 1 GiB (known read and
     write bytes), the reference against which the HBM traffic counters of the
@@ -508,6 +605,8 @@ def main():
         res, step, write = bench_copy(args)
     elif args.workload == "single":
         res, step, write = bench_sweep(args, pka, contexts=(128,), name="single")
+    elif args.workload == "rope_kv_write":
+        res, step, write = bench_rope(args, pka)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
 
@@ -528,7 +627,9 @@ def main():
     out.update(res)
     if isinstance(out.get("roofline"), dict):
         out["roofline"]["traffic"] = recorded_traffic(args.workload)
-    if not args.no_cpu_baseline and step is not None:
+    if "cpu_baseline" in out:
+        pass  # the workload timed its own oracle sample
+    elif not args.no_cpu_baseline and step is not None:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline_decode(step, write, args.cpu_seconds)
     else:
