@@ -50,10 +50,10 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # (profiles/traffic_fetch_write.md), valid only for the kernel source they were
 # taken on: (source file, sha256 prefix, bytes).
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode.hip", "9c1bf97e7ff6dd8e", 1189270016),
-    "splitk": ("decode.hip", "9c1bf97e7ff6dd8e", 270959840),
+    "decode_step": ("decode.hip", "8a05a50f968a9eee", 1189299152),
+    "splitk": ("decode.hip", "8a05a50f968a9eee", 270924752),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
-    "mixed": ("prefill.hip", "43dc6198ff6a4746", 45908160),
+    "mixed": ("prefill.hip", "4cce4cf0560dbad5", 45918208),
 }
 
 
@@ -81,6 +81,8 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-arms", action="store_true",
+                   help="skip the comparison arms (unified prefill, eager rotary) - for profiling the kernels alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP-graph replay)")
     return p.parse_args()
@@ -331,6 +333,16 @@ def bench_mixed(args, pka):
                                   prepare=True) for r in range(P.R)]
     pres = [pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, mcl, out=op, workspace=pws,
                                    prepare=True) for r in range(P.R)]
+    # "Unified" comparison arm (mini_engine, "Custom CUDA kernels"): every row,
+    # decodes included as one-row chunks, through the prefill kernel.  Timed
+    # beside the step, not part of it.
+    qsl_all = torch.cat([torch.arange(nd, dtype=torch.int32), nd + step.query_start_loc]).to(P.q.device)
+    mcl_all = int(step.context_lens.max())
+    uws = torch.empty(max(1, pka.prefill_workspace_bytes(S + step.num_prefill, P.q.shape[0], Hq, step.num_kv_heads, D,
+                                                         mcl_all)), dtype=torch.uint8, device="cuda:0")
+    uout = torch.empty_like(P.q)
+    unis = [pka.paged_attn_prefill(P.q, P.k[r], P.v[r], P.bt, P.cl, qsl_all, step.scale, mql, mcl_all, out=uout,
+                                   workspace=uws, prepare=True) for r in range(P.R)]
 
     def launch(i, ev):
         r = i % P.R
@@ -345,8 +357,14 @@ def bench_mixed(args, pka):
         pres[r]()
         if ev:
             ev[3].record()
+            if not args.no_arms:
+                unis[r]()
+            ev[4].record()
 
-    wall_ms, (write_ms, dec_ms, pre_ms) = timed_loop(launch, 3, args.steps, args.warmup)
+    # The wall clock covers the step only on warm-up passes (ev is None); the
+    # timed passes also run the unified arm, so the step time is the event sum.
+    _, (write_ms, dec_ms, pre_ms, uni_ms) = timed_loop(launch, 4, args.steps, args.warmup)
+    wall_ms = write_ms + dec_ms + pre_ms
     dbytes = W.decode_bytes(step)
     wbytes = W.kv_write_bytes(step)
     pbytes = W.prefill_bytes(step)
@@ -363,6 +381,8 @@ def bench_mixed(args, pka):
         "decode_GBps": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
         "prefill_us_per_call": round(pre_ms * 1e3, 2),
         "prefill_TFLOPs": round(tflops, 1),
+        "unified_arm_us_per_call": None if args.no_arms else round(uni_ms * 1e3, 2),
+        "unified_vs_split_attention": None if args.no_arms else round(uni_ms / (dec_ms + pre_ms), 2),
         "dtype": "bf16",
         "config": {
             "workload": "mixed paged step: KV write of 2048 rows, 64 decodes (ctx U[128,2048]) and ragged causal "
@@ -520,7 +540,8 @@ def bench_rope(args, pka):
         fused()
         if ev:
             ev[1].record()
-        eager()
+        if not args.no_arms:
+            eager()
         if ev:
             ev[2].record()
 
@@ -533,7 +554,7 @@ def bench_rope(args, pka):
         "unit": "GB/s",
         "ms_per_step": round(fused_ms, 4),
         "fused_us_per_call": round(fused_ms * 1e3, 2),
-        "eager_arm_us_per_call": round(eager_ms * 1e3, 2),
+        "eager_arm_us_per_call": None if args.no_arms else round(eager_ms * 1e3, 2),
         "dtype": "bf16",
         "config": {
             "workload": "fused rotary embedding + KV-cache write of the mixed step's 2048 new rows, bf16, 16q/8kv, "

@@ -27,8 +27,8 @@ int32_t elem_size(int32_t dtype) { return 2; }
 int32_t check_cache(const pka_cache_desc& c) {
   if (c.num_blocks <= 0 || c.block_size <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0) return PKA_ERR_SHAPE;
   if (c.dtype != PKA_F16 && c.dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
-  if (c.block_size != 16) return PKA_ERR_UNSUPPORTED;
-  if (c.head_dim != 64 && c.head_dim != 128) return PKA_ERR_UNSUPPORTED;
+  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32) return PKA_ERR_UNSUPPORTED;
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) return PKA_ERR_UNSUPPORTED;
   return PKA_OK;
 }
 
@@ -71,6 +71,7 @@ int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, 
   a->group = group;
   a->head_dim = cache.head_dim;
   a->max_blocks_per_seq = max_blocks_per_seq;
+  a->block_size = cache.block_size;
   a->scale = scale;
   a->bf16 = cache.dtype == PKA_BF16;
   return PKA_OK;
@@ -219,7 +220,7 @@ int32_t pka_paged_attn_splitk_reduce(const float* tmp_out, const float* max_logi
   if (num_seqs == 0) return PKA_OK;
   if (!tmp_out || !max_logits || !exp_sums || !context_lens || !out) return PKA_ERR_NULL;
   if (dtype != PKA_F16 && dtype != PKA_BF16) return PKA_ERR_UNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PKA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKA_ERR_UNSUPPORTED;
   if (partition_size != pka::kPartitionSize) return PKA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
   pka::ReduceArgs a{};
@@ -333,7 +334,8 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   if (st) return st;
   if (max_blocks_per_seq <= 0 || max_query_len == 0 || max_query_len > num_q_tokens) return PKA_ERR_SHAPE;
   if (max_context_len < max_query_len) return PKA_ERR_SHAPE;
-  if (!pka::prefill_supported(cache.dtype == PKA_BF16, cache.head_dim, group)) return PKA_ERR_UNSUPPORTED;
+  if (!pka::prefill_supported(cache.dtype == PKA_BF16, cache.head_dim, group, cache.block_size))
+    return PKA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || !std::isfinite(scale)) return PKA_ERR_UNSUPPORTED;  // the running max assumes scale > 0
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKA_ERR_ALIGN;
   const size_t need = pka_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, cache.num_kv_heads,
@@ -357,6 +359,7 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   a.group = group;
   a.head_dim = cache.head_dim;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = cache.block_size;
   a.scale = scale;
   a.bf16 = cache.dtype == PKA_BF16;
   a.out = static_cast<uint16_t*>(out);

@@ -14,7 +14,8 @@
 // Lane layout inside a wavefront.  One 16-byte load per lane (8 elements)
 // makes a token row of D elements span LPT = D / 8 lanes, so one wave load
 // covers TPL = 64 / LPT tokens and a 16-token block of one head takes
-// LPB = 16 / TPL loads per tensor (D = 128: 16 lanes, 4 tokens, 4 loads).
+// LPB = 16 / TPL loads per tensor (D = 128: 16 lanes, 4 tokens, 4 loads);
+// 8- and 32-token blocks take half and twice as many.
 // Each group of LPT lanes ("row") sums its dot-product pieces with DPP and
 // keeps its own online-softmax state (max, exp-sum, 8 accumulator dims per
 // head) over the tokens it sees; rows, then wavefronts, are merged once at the
@@ -41,17 +42,16 @@
 
 namespace pka {
 
-constexpr int kBlockSize = 16;
-
-template <int D>
+template <int D, int BS>
 struct DecodeLayout {
   static constexpr int LPT = D / 8;       // lanes per token row
   static constexpr int TPL = kWave / LPT;  // token rows per wave load
-  static constexpr int LPB = kBlockSize / TPL;  // wave loads per block per tensor
-  static_assert(kWave % LPT == 0 && kBlockSize % TPL == 0, "unsupported head_dim");
+  static constexpr int LPB = BS / TPL;     // wave loads per block per tensor
+  static_assert(kWave % LPT == 0 && BS % TPL == 0 && kPartitionSize % BS == 0, "unsupported head_dim / block");
 };
 
-template <typename T, int D, int G, int W, bool SPLIT>
+// BS = tokens per KV block (8, 16 or 32).
+template <typename T, int D, int G, int W, bool SPLIT, int BS>
 __global__ void __launch_bounds__(W * kWave)
 paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -59,7 +59,8 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int32_t num_kv_heads, float scale_log2, uint16_t* __restrict__ out,
                     float* __restrict__ tmp_out, float* __restrict__ max_logits,
                     float* __restrict__ exp_sums, int32_t max_num_partitions) {
-  using L = DecodeLayout<D>;
+  using L = DecodeLayout<D, BS>;
+  constexpr int kBlockSize = BS;
   using E = Elem<T>;
   constexpr int LPT = L::LPT, TPL = L::TPL, LPB = L::LPB;
 
@@ -370,17 +371,17 @@ constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per single-pass de
 #endif
 constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partition workgroup
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int BS>
 static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t stream) {
   const float scale_log2 = a.scale * kLog2e;
   if (!split) {
     dim3 grid(a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, false>), grid, dim3(kDecodeWaves * kWave), 0,
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, false, BS>), grid, dim3(kDecodeWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0);
   } else {
     dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true>), grid, dim3(kSplitWaves * kWave), 0,
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true, BS>), grid, dim3(kSplitWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, nullptr, a.tmp_out, a.max_logits, a.exp_sums,
                        a.max_num_partitions);
@@ -388,26 +389,39 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t s
   return hipGetLastError();
 }
 
+template <typename T, int D, int G>
+static hipError_t launch_decode_b(const DecodeArgs& a, bool split, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_decode_t<T, D, G, 8>(a, split, stream);
+    case 16: return launch_decode_t<T, D, G, 16>(a, split, stream);
+    case 32: return launch_decode_t<T, D, G, 32>(a, split, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int D>
 static hipError_t launch_decode_g(const DecodeArgs& a, bool split, hipStream_t stream) {
   switch (a.group) {
-    case 1: return launch_decode_t<T, D, 1>(a, split, stream);
-    case 2: return launch_decode_t<T, D, 2>(a, split, stream);
-    case 4: return launch_decode_t<T, D, 4>(a, split, stream);
-    case 8: return launch_decode_t<T, D, 8>(a, split, stream);
+    case 1: return launch_decode_b<T, D, 1>(a, split, stream);
+    case 2: return launch_decode_b<T, D, 2>(a, split, stream);
+    case 4: return launch_decode_b<T, D, 4>(a, split, stream);
+    case 8: return launch_decode_b<T, D, 8>(a, split, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_decode_d(const DecodeArgs& a, bool split, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_decode_g<T, 64>(a, split, stream);
+    case 128: return launch_decode_g<T, 128>(a, split, stream);
+    case 256: return launch_decode_g<T, 256>(a, split, stream);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream) {
-  if (a.bf16) {
-    if (a.head_dim == 64) return launch_decode_g<BF16, 64>(a, split, stream);
-    if (a.head_dim == 128) return launch_decode_g<BF16, 128>(a, split, stream);
-  } else {
-    if (a.head_dim == 64) return launch_decode_g<F16, 64>(a, split, stream);
-    if (a.head_dim == 128) return launch_decode_g<F16, 128>(a, split, stream);
-  }
-  return hipErrorInvalidValue;
+  return a.bf16 ? launch_decode_d<BF16>(a, split, stream) : launch_decode_d<F16>(a, split, stream);
 }
 
 hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream) {
@@ -419,10 +433,12 @@ hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream) {
   if (a.bf16) {
     if (a.head_dim == 64) PKA_REDUCE(BF16, 64);
     else if (a.head_dim == 128) PKA_REDUCE(BF16, 128);
+    else if (a.head_dim == 256) PKA_REDUCE(BF16, 256);
     else return hipErrorInvalidValue;
   } else {
     if (a.head_dim == 64) PKA_REDUCE(F16, 64);
     else if (a.head_dim == 128) PKA_REDUCE(F16, 128);
+    else if (a.head_dim == 256) PKA_REDUCE(F16, 256);
     else return hipErrorInvalidValue;
   }
 #undef PKA_REDUCE

@@ -27,6 +27,7 @@ struct DecodeArgs {
   int32_t group;  // query heads per KV head
   int32_t head_dim;
   int32_t max_blocks_per_seq;
+  int32_t block_size;          // tokens per KV block: 8, 16 or 32
   int32_t max_num_partitions;  // split-K only
   float scale;
   bool bf16;
@@ -75,6 +76,7 @@ struct PrefillArgs {
   int32_t group;
   int32_t head_dim;
   int32_t max_blocks_per_seq;
+  int32_t block_size;  // tokens per KV block: 8, 16 or 32
   float scale;
   bool bf16;
   uint16_t* out;
@@ -100,7 +102,7 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(float* table, int max_position, int head_dim, double theta, hipStream_t stream);
 hipError_t launch_rope_kv_write(const RopeKvArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-bool prefill_supported(bool bf16, int head_dim, int group);
+bool prefill_supported(bool bf16, int head_dim, int group, int block_size);
 size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
                                 int max_context_len);
 

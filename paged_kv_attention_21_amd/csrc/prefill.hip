@@ -88,7 +88,6 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfRowsPerWave = 32;    // two 16-row MFMA tiles
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // q-rows per query tile (positions x group heads)
 constexpr int kPfKeys = 32;           // keys per staged tile (two KV blocks)
-constexpr int kPfBlock = 16;          // KV block size
 // Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
 // swizzle, no stride).  Loads use offsets well inside num_records.
 constexpr int kBufferFlags = 0x00020000;
@@ -182,7 +181,8 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
   return true;
 }
 
-template <typename T, int D, int G>
+// BS = tokens per KV block (8, 16 or 32): a 32-key tile spans 32 / BS blocks.
+template <typename T, int D, int G, int BS>
 __global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -266,8 +266,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   uint4 kreg_a[PER], kreg_b[PER], vreg_a[PER], vreg_b[PER];  // two prefetch sets per tensor
   const int my_row = threadIdx.x / (D / 8);           // row of pass 0
   const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
-  const uint32_t goff = (uint32_t)((my_row % kPfBlock) * row_elems + (size_t)kvh * D + my_col);  // elements
-  const size_t blk_elems = (size_t)kPfBlock * row_elems;
+  const size_t blk_elems = (size_t)BS * row_elems;
   // A block past the context is replaced by the context's last block (only
   // table entries inside the context are read): its rows are fetched from
   // memory the sequence owns and then zeroed.
@@ -278,22 +277,28 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // is the descriptor plus its own constant byte offset and no per-lane
   // address arithmetic is left in the loop.
   const int32_t* __restrict__ tbl_row = block_tables + (size_t)tl.seq * max_blocks_per_seq;
-  const int lb_last = (ctx - 1) / kPfBlock;  // last logical block inside the context
-  const uint32_t goff_bytes = goff * 2u;
+  const int lb_last = (ctx - 1) / BS;  // last logical block inside the context
+  // Byte offset of pass r's piece inside its block (the row's offset in the
+  // block, then the head and the dims).
+  uint32_t goff_bytes[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r)
+    goff_bytes[r] = (uint32_t)((((my_row + r * ROWS_PER_PASS) % BS) * row_elems + (size_t)kvh * D + my_col) * 2);
   auto fetch = [&](const uint16_t* __restrict__ cache, int tile, uint4 (&reg)[PER]) {
     if (!mover) return;  // whole wavefronts (rows past the tile)
     const int k0 = k_lo + tile * kPfKeys;
-    const int lb0 = k0 / kPfBlock;
-    const int pb0 = tbl_row[lb0];
-    const int pb1 = tbl_row[min(lb0 + 1, lb_last)];
+    const int lb0 = k0 / BS;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      // KV block of this pass: 0 or 1, the same for the whole wavefront.
-      const int blk_of = __builtin_amdgcn_readfirstlane((my_row + r * ROWS_PER_PASS) / kPfBlock);
-      const uint16_t* base = cache + (size_t)(blk_of == 0 ? pb0 : pb1) * blk_elems;
+      // KV block of this pass inside the tile: the same for the whole
+      // wavefront (its kWave / (D/8) rows never straddle a block boundary),
+      // so it follows from the scalar wavefront index alone.
+      const int blk_of = (wave * (kWave / (D / 8)) + r * ROWS_PER_PASS) / BS;
+      const int pb = tbl_row[min(lb0 + blk_of, lb_last)];
+      const uint16_t* base = cache + (size_t)pb * blk_elems;
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, 0x7fffffff, kBufferFlags);
-      reg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, goff_bytes, 0, 0));
+      reg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, goff_bytes[r], 0, 0));
     }
     if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
@@ -607,13 +612,13 @@ size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads
   return prefill_tiles_upper_bound(num_q_tokens, num_seqs, group) * splits * num_kv_heads * pf_slot_floats(head_dim);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int BS>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const size_t tiles = prefill_tiles_upper_bound(a.num_q_tokens, a.num_seqs, G);
   const int splits = (a.max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
   if (tiles > 65535 || splits > 65535) return hipErrorInvalidValue;
   dim3 grid(a.num_kv_heads, (unsigned)tiles, (unsigned)splits);
-  hipLaunchKernelGGL((paged_prefill_kernel<T, D, G>), grid, dim3(kPfThreads), 0, stream, a.q, a.k_cache, a.v_cache,
+  hipLaunchKernelGGL((paged_prefill_kernel<T, D, G, BS>), grid, dim3(kPfThreads), 0, stream, a.q, a.k_cache, a.v_cache,
                      a.block_tables, a.context_lens, a.query_start_loc, a.num_seqs, a.max_blocks_per_seq,
                      a.num_kv_heads, splits, a.scale * kLog2e, a.out, a.workspace);
   hipError_t e = hipGetLastError();
@@ -625,19 +630,30 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
-  switch (a.group) {
-    case 1: return launch_prefill_t<T, D, 1>(a, stream);
-    case 2: return launch_prefill_t<T, D, 2>(a, stream);
-    case 4: return launch_prefill_t<T, D, 4>(a, stream);
-    case 8: return launch_prefill_t<T, D, 8>(a, stream);
+template <typename T, int D, int G>
+static hipError_t launch_prefill_b(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.block_size) {
+    case 8: return launch_prefill_t<T, D, G, 8>(a, stream);
+    case 16: return launch_prefill_t<T, D, G, 16>(a, stream);
+    case 32: return launch_prefill_t<T, D, G, 32>(a, stream);
   }
   return hipErrorInvalidValue;
 }
 
-bool prefill_supported(bool bf16, int head_dim, int group) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+template <typename T, int D>
+static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.group) {
+    case 1: return launch_prefill_b<T, D, 1>(a, stream);
+    case 2: return launch_prefill_b<T, D, 2>(a, stream);
+    case 4: return launch_prefill_b<T, D, 4>(a, stream);
+    case 8: return launch_prefill_b<T, D, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool prefill_supported(bool bf16, int head_dim, int group, int block_size) {
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
+         (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

@@ -63,7 +63,7 @@ def test_kv_write_validation(pka):
     assert lib.pka_kv_cache_write(A, A, A, 0, A, A, d, None) == 0  # empty: no-op
     assert lib.pka_kv_cache_write(None, A, A, 4, A, A, d, None) == 1
     assert lib.pka_kv_cache_write(A + 2, A, A, 4, A, A, d, None) == 4
-    assert lib.pka_kv_cache_write(A, A, A, 4, A, A, _desc(pka, bs=8), None) == 3
+    assert lib.pka_kv_cache_write(A, A, A, 4, A, A, _desc(pka, bs=64), None) == 3
     assert lib.pka_kv_cache_write(A, A, A, 4, A, A, _desc(pka, d=96), None) == 3
     assert lib.pka_kv_cache_write(A, A, A, 4, A, A, _desc(pka, dt=7), None) == 3
     assert lib.pka_kv_cache_write(A, A, A, 4, A, A, _desc(pka, nb=0), None) == 2
@@ -104,7 +104,8 @@ def test_prefill_validation(pka):
     assert pf(A, A, A, A, A, A, 2, 10, 11, 100, 16, 8, 0.1, A, d, None, 0, None) == 2  # max_query_len > num_q_tokens
     assert pf(A, A, A, A, A, A, 2, 10, 5, 4, 16, 8, 0.1, A, d, None, 0, None) == 2     # max_context_len < max_query_len
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 12, 8, 0.1, A, d, None, 0, None) == 2   # 12 % 8
-    bad = _desc(pka, bs=32, hkv=8, d=128, dt=1)
+    bad = _desc(pka, bs=64, hkv=8, d=128, dt=1)
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, _desc(pka, hkv=8, d=256, dt=1), None, 0, None) == 3
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, bad, None, 0, None) == 3
     for scale in (0.0, -0.1, float("inf"), float("nan")):  # the running max assumes a positive scale
         assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, scale, A, d, None, 0, None) == 3

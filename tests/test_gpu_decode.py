@@ -187,3 +187,35 @@ def test_empty_batch_is_noop(pka):
 
 def test_tolerances_are_the_stated_ones():
     assert TOL[torch.float16] == 2e-3 and TOL[torch.bfloat16] == 1.5e-2
+
+
+# Block sizes other than 16 and head size 256 (mini_engine, "Roadmap":
+# generalising the kernels beyond one head shape).  (dtype, Hq, Hkv, D, block)
+GENERAL = [
+    (torch.bfloat16, 16, 8, 128, 8),
+    (torch.bfloat16, 16, 8, 128, 32),
+    (torch.float16, 2, 2, 64, 32),
+    (torch.float16, 8, 2, 64, 8),
+    (torch.bfloat16, 8, 8, 256, 16),
+    (torch.bfloat16, 16, 2, 256, 8),
+    (torch.float16, 4, 1, 256, 32),
+]
+
+
+@pytest.mark.parametrize("variant", ["v1", "v2"])
+@pytest.mark.parametrize("shape", GENERAL, ids=[f"{str(s[0])[6:]}-{s[1]}q{s[2]}kv-d{s[3]}-b{s[4]}" for s in GENERAL])
+def test_general_block_and_head_sizes(pka, shape, variant):
+    """Write-then-decode over ragged contexts (around block, partition and
+    window boundaries) for each block size / head size."""
+    dtype, hq, hkv, d, bs = shape
+    ctx = [1, bs - 1, bs, bs + 1, 255, 256, 257, 1000, 64 * bs + 3]
+    step = W.make_decode_step(context_lens=ctx, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                              block_size=bs, seed=9, poison=True, write_new=True)
+    ds = DevStep(step)
+    pka.kv_cache_write(ds.new_k, ds.new_v, ds.slot_mapping, ds.k_cache, ds.v_cache)
+    kc, vc = oracle.kv_cache_write(step.new_k, step.new_v, step.slot_mapping, step.k_cache, step.v_cache)
+    torch.cuda.synchronize()
+    assert torch.equal(ds.k_cache.cpu().view(torch.int16), kc.view(torch.int16)), "KV write not bit-exact"
+    assert torch.equal(ds.v_cache.cpu().view(torch.int16), vc.view(torch.int16)), "KV write not bit-exact"
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step, k_cache=kc, v_cache=vc), dtype, f"general {shape} {variant}")

@@ -177,3 +177,23 @@ def test_prefill_repeat_and_placement_bit_identity(pka):
     step.block_tables = perm[step.block_tables.long()].to(torch.int32)
     c = run_prefill(pka, DevStep(step))
     assert torch.equal(a.cpu().view(torch.int16), c.cpu().view(torch.int16)), "block relabelling changed bits"
+
+
+# Block sizes 8 and 32 (a 32-key staging tile then spans four or one blocks).
+GENERAL = [
+    (torch.bfloat16, 16, 8, 128, 8),
+    (torch.bfloat16, 16, 8, 128, 32),
+    (torch.float16, 8, 2, 64, 8),
+    (torch.float16, 8, 8, 64, 32),
+]
+
+
+@pytest.mark.parametrize("shape", GENERAL, ids=[f"{str(s[0])[6:]}-{s[1]}q{s[2]}kv-d{s[3]}-b{s[4]}" for s in GENERAL])
+def test_general_block_sizes(pka, shape):
+    dtype, hq, hkv, d, bs = shape
+    step = W.make_prefill_step(query_lens=[1, 31, 33, 64, 129, 200, 17], cached_lens=[0, 7, 1, 100, 40, 1100, 2047],
+                               dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, seed=38,
+                               poison=True, write_new=False)
+    ds = DevStep(step)
+    out = run_prefill(pka, ds)
+    assert_parity(out, oracle_prefill(step), dtype, f"prefill block size {shape}")
