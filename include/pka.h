@@ -262,6 +262,54 @@ size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32
  * first call), or a negative value if the HIP runtime fails. */
 int32_t pka_device_cu_count(void);
 
+/*
+ * Host-side paged block manager (MiniLLM Runtime: "Features" - block
+ * allocation, release, reuse, reference counting, prefix-cache lookup with
+ * shared ownership; mini_engine "Features": blocks hashed as soon as they
+ * fill; miniserve "Architecture": KVCacheManager with chained hashes,
+ * refcounts and an LRU free list, and its request-state diagram).  Pure host
+ * code, no GPU calls; one manager per KV pool, not thread-safe.
+ *
+ * Pages are reference counted; free pages form an LRU list (new pages from
+ * its front, pages reaching refcount 0 to its tail in block-table order).  A
+ * page that fills is registered under the chained hash of its token prefix
+ * and keeps that registration while free, until it is taken for new
+ * content.  Hits are confirmed against the stored tokens and parent hash.
+ *
+ * Request flow: add_request(prompt) -> admit(first chunk) -> [allocate(n) ->
+ * run the kernels on slot_mapping / block_table -> commit(n) ->
+ * append_token(sampled)]* -> free_request.  Return conventions: status codes
+ * (pka_status) for commands; counts or 1/0 (done / no room) for queries, with
+ * a negated pka_status on error.
+ */
+typedef struct pka_block_manager pka_block_manager;
+pka_block_manager* pka_bm_create(int32_t num_blocks, int32_t block_size); /* NULL on bad sizes / no memory */
+void pka_bm_destroy(pka_block_manager* m);
+int32_t pka_bm_num_free(const pka_block_manager* m);
+int32_t pka_bm_refcount(const pka_block_manager* m, int32_t block);
+/* Register a request and its prompt token ids (copied). */
+int32_t pka_bm_add_request(pka_block_manager* m, int64_t req_id, const int32_t* tokens, int32_t num_tokens);
+int32_t pka_bm_append_token(pka_block_manager* m, int64_t req_id, int32_t token);
+/* Pages of the longest cached whole-block prefix, always leaving >= 1 token to
+ * compute; writes up to max_blocks ids, returns their number. */
+int32_t pka_bm_find_cached_prefix(const pka_block_manager* m, int64_t req_id, int32_t* blocks, int32_t max_blocks);
+/* Prefix lookup + room for first_chunk more tokens, all or nothing: 1 and
+ * *num_cached_tokens set, or 0 when the pool cannot hold it (no change). */
+int32_t pka_bm_admit(pka_block_manager* m, int64_t req_id, int32_t first_chunk, int32_t* num_cached_tokens);
+/* Room for num_new_tokens past the computed ones: 1, or 0 (no change). */
+int32_t pka_bm_allocate(pka_block_manager* m, int64_t req_id, int32_t num_new_tokens);
+/* num_tokens more tokens now have K/V in the pool; filled pages get registered. */
+int32_t pka_bm_commit(pka_block_manager* m, int64_t req_id, int32_t num_tokens);
+/* Drop the request's pages (refcount - 1); keep_request != 0 keeps its tokens
+ * with nothing computed (preemption), else forgets it. */
+int32_t pka_bm_free_request(pka_block_manager* m, int64_t req_id, int32_t keep_request);
+/* The request's block table (page ids in logical order); returns its length. */
+int32_t pka_bm_block_table(const pka_block_manager* m, int64_t req_id, int32_t* out, int32_t max_blocks);
+/* slot = page * block_size + offset for logical positions start .. start+n-1. */
+int32_t pka_bm_slot_mapping(const pka_block_manager* m, int64_t req_id, int32_t start, int32_t num_tokens,
+                            int64_t* out);
+int32_t pka_bm_num_computed(const pka_block_manager* m, int64_t req_id);
+
 #ifdef __cplusplus
 }
 #endif

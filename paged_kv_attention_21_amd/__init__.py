@@ -10,6 +10,7 @@ importing the package without the built library raises ImportError.
 from ._lib import (  # noqa: F401
     LIB_PATH,
     PARTITION_SIZE,
+    BlockManager,
     CacheDesc,
     PkaError,
     Prepared,

@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 # PKA_LIBRARY may point at another build of the same library (e.g. a tuning variant).
@@ -88,6 +89,20 @@ _SIGNATURES = {
     "pka_prefill_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pka_rope_table": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "pka_rope_table_bytes": (c_size_t, [c_int32, c_int32]),
+    "pka_bm_create": (c_void_p, [c_int32, c_int32]),
+    "pka_bm_destroy": (None, [c_void_p]),
+    "pka_bm_num_free": (c_int32, [c_void_p]),
+    "pka_bm_refcount": (c_int32, [c_void_p, c_int32]),
+    "pka_bm_add_request": (c_int32, [c_void_p, ctypes.c_int64, c_void_p, c_int32]),
+    "pka_bm_append_token": (c_int32, [c_void_p, ctypes.c_int64, c_int32]),
+    "pka_bm_find_cached_prefix": (c_int32, [c_void_p, ctypes.c_int64, c_void_p, c_int32]),
+    "pka_bm_admit": (c_int32, [c_void_p, ctypes.c_int64, c_int32, ctypes.POINTER(c_int32)]),
+    "pka_bm_allocate": (c_int32, [c_void_p, ctypes.c_int64, c_int32]),
+    "pka_bm_commit": (c_int32, [c_void_p, ctypes.c_int64, c_int32]),
+    "pka_bm_free_request": (c_int32, [c_void_p, ctypes.c_int64, c_int32]),
+    "pka_bm_block_table": (c_int32, [c_void_p, ctypes.c_int64, c_void_p, c_int32]),
+    "pka_bm_slot_mapping": (c_int32, [c_void_p, ctypes.c_int64, c_int32, c_int32, c_void_p]),
+    "pka_bm_num_computed": (c_int32, [c_void_p, ctypes.c_int64]),
     "pka_fused_rope_kv_write": (
         c_int32,
         [c_void_p, ctypes.c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
@@ -220,6 +235,77 @@ def kv_cache_write(key, value, slot_mapping, k_cache, v_cache, prepare=False):
     return _launch(lib.pka_kv_cache_write,
                    (_ptr(key), _ptr(value), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cache_desc(k_cache),
                     _stream(k_cache)), prepare, (key, value, slot_mapping, k_cache, v_cache))
+
+
+class BlockManager:
+    """Host paged block manager (the library's C++ one): refcounted pages, an
+    LRU free list and a whole-block prefix cache; produces the block tables
+    and slot mappings the kernels take.  Token ids and outputs are numpy
+    int32 / int64 arrays (host memory)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self._h = lib.pka_bm_create(self.num_blocks, self.block_size)
+        if not self._h:
+            raise ValueError("bad block-manager sizes")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib.pka_bm_destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _neg(ret):
+        if ret < 0:
+            _check(-ret)
+        return ret
+
+    def num_free(self) -> int:
+        return lib.pka_bm_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return lib.pka_bm_refcount(self._h, int(block))
+
+    def add_request(self, rid: int, tokens) -> None:
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        _check(lib.pka_bm_add_request(self._h, int(rid), t.ctypes.data_as(c_void_p), int(t.size)))
+
+    def append_token(self, rid: int, token: int) -> None:
+        _check(lib.pka_bm_append_token(self._h, int(rid), int(token)))
+
+    def find_cached_prefix(self, rid: int) -> list[int]:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = self._neg(lib.pka_bm_find_cached_prefix(self._h, int(rid), out.ctypes.data_as(c_void_p), out.size))
+        return out[:n].tolist()
+
+    def admit(self, rid: int, first_chunk: int):
+        """Number of cached tokens, or None when the pool has no room."""
+        cached = c_int32(0)
+        ok = self._neg(lib.pka_bm_admit(self._h, int(rid), int(first_chunk), ctypes.byref(cached)))
+        return cached.value if ok else None
+
+    def allocate(self, rid: int, n: int) -> bool:
+        return bool(self._neg(lib.pka_bm_allocate(self._h, int(rid), int(n))))
+
+    def commit(self, rid: int, n: int) -> None:
+        _check(lib.pka_bm_commit(self._h, int(rid), int(n)))
+
+    def free_request(self, rid: int, drop: bool = True) -> None:
+        _check(lib.pka_bm_free_request(self._h, int(rid), 0 if drop else 1))
+
+    def block_table(self, rid: int) -> list[int]:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = self._neg(lib.pka_bm_block_table(self._h, int(rid), out.ctypes.data_as(c_void_p), out.size))
+        return out[:n].tolist()
+
+    def slot_mapping(self, rid: int, start: int, n: int) -> np.ndarray:
+        out = np.empty(max(int(n), 1), dtype=np.int64)
+        _check(lib.pka_bm_slot_mapping(self._h, int(rid), int(start), int(n), out.ctypes.data_as(c_void_p)))
+        return out[: int(n)]
+
+    def computed(self, rid: int) -> int:
+        return self._neg(lib.pka_bm_num_computed(self._h, int(rid)))
 
 
 def rope_table(max_position, head_dim, theta, device):

@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(ROOT, "_build", "pka")
 LIB_NAME = "libpka.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "rope_kv.hip"]
+SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "rope_kv.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
