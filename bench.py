@@ -32,6 +32,7 @@ import os
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -77,7 +78,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_step",
-                   choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write"])
+                   choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write",
+                            "block_manager"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
@@ -571,6 +573,128 @@ def bench_rope(args, pka):
     return res, None, False
 
 
+def block_manager_trace(seed, steps, budget=2048, num_blocks=20000, block_size=16):
+    """A chunked-prefill serving trace as host operations: each step
+    schedules the running decodes, then continues or admits prompts in chunks
+    until the token budget is used (prompts 90% U[128,512] / 10% U[4096,7680],
+    30% sharing one 256-token prefix, outputs U[16,256] tokens)."""
+    rng = np.random.default_rng(seed)
+    prefix = rng.integers(0, 150000, size=256).tolist()
+    ops, rid = [], 0
+    live = {}  # rid -> [prompt_len, computed, to_generate]
+    waiting = []
+    for _ in range(steps):
+        left = budget
+        step = []
+        for r in list(live):
+            plen, comp, gen = live[r]
+            if comp >= plen and left > 0:  # decode
+                step.append(("decode", r))
+                left -= 1
+                live[r][2] -= 1
+                if live[r][2] <= 0:
+                    step.append(("finish", r))
+                    del live[r]
+        while left > 0:
+            if not waiting:
+                rid += 1
+                P = int(rng.integers(4096, 7681)) if rng.random() < 0.1 else int(rng.integers(128, 513))
+                toks = (prefix if rng.random() < 0.3 and P > 256 else []) + rng.integers(0, 150000, size=P).tolist()
+                waiting.append((rid, toks, int(rng.integers(16, 257))))
+            r, toks, gen = waiting.pop(0)
+            n = min(len(toks), left, 512)
+            step.append(("admit", r, toks, n))
+            left -= n
+            if n < len(toks):
+                step.append(("chunks", r, len(toks) - n))
+            live[r] = [len(toks), len(toks), gen]
+        ops.append(step)
+    return ops, num_blocks, block_size
+
+
+def run_block_manager_trace(mgr, ops, rng_seed=0):
+    """Replay a trace through a manager (library or reference); returns the
+    number of tokens scheduled.  A step's decodes go through one batched call
+    when the manager has it."""
+    rng = np.random.default_rng(rng_seed)
+    tokens = 0
+    alive = set()  # admitted requests (the trace was drawn without knowing which fit)
+    batched = hasattr(mgr, "decode_step")
+    for step in ops:
+        dec = [op[1] for op in step if op[0] == "decode" and op[1] in alive]
+        toks = rng.integers(0, 150000, size=len(dec)).tolist()
+        if batched and dec:
+            _, ok = mgr.decode_step(dec, toks)
+            tokens += int(ok.sum())
+        else:
+            for r, t in zip(dec, toks):
+                mgr.append_token(r, t)
+                if mgr.allocate(r, 1):
+                    mgr.commit(r, 1)
+                    tokens += 1
+        for op in step:
+            kind, r = op[0], op[1]
+            if kind == "finish" and r in alive:
+                mgr.free_request(r)
+                alive.discard(r)
+            elif kind == "admit":
+                toks, n = op[2], op[3]
+                mgr.add_request(r, toks)
+                cached = mgr.admit(r, n)
+                if cached is None:
+                    mgr.free_request(r)
+                    continue
+                alive.add(r)
+                step_n = min(n, len(toks) - cached)
+                mgr.commit(r, step_n)
+                tokens += step_n
+                rest = len(toks) - cached - step_n
+                while rest > 0:  # later chunks of the same prompt
+                    c = min(rest, 512)
+                    if not mgr.allocate(r, c):
+                        break
+                    mgr.commit(r, c)
+                    tokens += c
+                    rest -= c
+    return tokens
+
+
+def bench_block_manager(args, pka):
+    """Host workload on the same data structure the kernels read: the
+    library's C++ block manager replaying a chunked-prefill serving trace."""
+    ops, N, B = block_manager_trace(args.seed, max(args.steps, 1) * 20)
+    warm = pka.BlockManager(N, B)
+    run_block_manager_trace(warm, ops[: max(1, len(ops) // 10)])
+    mgr = pka.BlockManager(N, B)
+    t0 = time.perf_counter()
+    tokens = run_block_manager_trace(mgr, ops)
+    el = time.perf_counter() - t0
+    res = {
+        "metric": "block-manager scheduled tokens/s (host, one core)",
+        "value": round(tokens / el, 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(el * 1e3 / len(ops), 4),
+        "higher_is_better": True,
+        "dtype": "int32",
+        "config": {"workload": f"chunked-prefill serving trace through the C++ block manager: {len(ops)} steps of "
+                               f"budget 2048, {N} pages of {B} tokens, prompts 90% U[128,512] / 10% U[4096,7680], "
+                               "30% sharing a 256-token prefix", "tokens": tokens, "seed": args.seed},
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle.block_manager import RefBlockManager
+
+        sample = ops[: max(1, len(ops) // 4)]
+        ref = RefBlockManager(N, B)
+        t0 = time.perf_counter()
+        rt = run_block_manager_trace(ref, sample)
+        rel = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(rt / rel, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the Python reference manager on the first {len(sample)} steps "
+                                         f"({rt} tokens in {rel:.2f} s)"}
+    return res, None, False
+
+
 def bench_copy(args):
     """Calibration: a plain device-to-device copy of 1 GiB (known read and
     write bytes), the reference against which the HBM traffic counters of the
@@ -608,12 +732,14 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this library has no multi-GPU path.", flush=True)
         sys.exit(2)
-    if not torch.cuda.is_available():
+    host_only = args.workload == "block_manager"  # host data structure, no kernels
+    if not host_only and not torch.cuda.is_available():
         print("bench.py needs a GPU", flush=True)
         sys.exit(1)
     import paged_kv_attention_21_amd as pka
 
-    torch.cuda.set_device(0)
+    if torch.cuda.is_available():
+        torch.cuda.set_device(0)
     if args.workload == "decode_step":
         res, step, write = bench_decode_step(args, pka)
     elif args.workload == "splitk":
@@ -628,6 +754,8 @@ def main():
         res, step, write = bench_sweep(args, pka, contexts=(128,), name="single")
     elif args.workload == "rope_kv_write":
         res, step, write = bench_rope(args, pka)
+    elif args.workload == "block_manager":
+        res, step, write = bench_block_manager(args, pka)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
 
@@ -655,7 +783,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline_decode(step, write, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
-    out["gpu"] = fingerprint()
+    out["gpu"] = fingerprint() if torch.cuda.is_available() else None
     print(json.dumps(out), flush=True)
 
 

@@ -309,6 +309,13 @@ int32_t pka_bm_block_table(const pka_block_manager* m, int64_t req_id, int32_t* 
 int32_t pka_bm_slot_mapping(const pka_block_manager* m, int64_t req_id, int32_t start, int32_t num_tokens,
                             int64_t* out);
 int32_t pka_bm_num_computed(const pka_block_manager* m, int64_t req_id);
+/* One decode step for num_reqs running requests in one call: append
+ * tokens[i] to request req_ids[i], make room for it, write its slot to
+ * slots[i] and count it computed (ok[i] = 1), or leave the request unchanged
+ * apart from the appended token when the pool is full (ok[i] = 0, slots[i] =
+ * -1, a padded row for the KV write).  Returns the number of rows placed. */
+int32_t pka_bm_decode_step(pka_block_manager* m, int32_t num_reqs, const int64_t* req_ids, const int32_t* tokens,
+                           int64_t* slots, int32_t* ok);
 
 #ifdef __cplusplus
 }

@@ -103,6 +103,7 @@ _SIGNATURES = {
     "pka_bm_block_table": (c_int32, [c_void_p, ctypes.c_int64, c_void_p, c_int32]),
     "pka_bm_slot_mapping": (c_int32, [c_void_p, ctypes.c_int64, c_int32, c_int32, c_void_p]),
     "pka_bm_num_computed": (c_int32, [c_void_p, ctypes.c_int64]),
+    "pka_bm_decode_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "pka_fused_rope_kv_write": (
         c_int32,
         [c_void_p, ctypes.c_int64, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
@@ -306,6 +307,20 @@ class BlockManager:
 
     def computed(self, rid: int) -> int:
         return self._neg(lib.pka_bm_num_computed(self._h, int(rid)))
+
+    def decode_step(self, rids, tokens):
+        """Append one token to each running request, place it and count it
+        computed, in one call.  Returns (slots int64, ok bool); a request the
+        pool cannot hold gets slot -1 and ok False (only its token appended)."""
+        r = np.ascontiguousarray(np.asarray(rids, dtype=np.int64))
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        if r.shape != t.shape:
+            raise ValueError("one token per request")
+        slots = np.empty(max(r.size, 1), dtype=np.int64)
+        ok = np.empty(max(r.size, 1), dtype=np.int32)
+        self._neg(lib.pka_bm_decode_step(self._h, int(r.size), r.ctypes.data_as(c_void_p), t.ctypes.data_as(c_void_p),
+                                         slots.ctypes.data_as(c_void_p), ok.ctypes.data_as(c_void_p)))
+        return slots[: r.size], ok[: r.size].astype(bool)
 
 
 def rope_table(max_position, head_dim, theta, device):

@@ -285,6 +285,32 @@ int32_t pka_bm_slot_mapping(const pka_block_manager* m, int64_t req_id, int32_t 
   return PKA_OK;
 }
 
+int32_t pka_bm_decode_step(pka_block_manager* m, int32_t num_reqs, const int64_t* req_ids, const int32_t* tokens,
+                           int64_t* slots, int32_t* ok) {
+  if (!m || num_reqs < 0 || (num_reqs > 0 && (!req_ids || !tokens || !slots || !ok))) return -PKA_ERR_NULL;
+  int32_t done = 0;
+  for (int32_t i = 0; i < num_reqs; ++i) {
+    auto it = m->reqs.find(req_ids[i]);
+    if (it == m->reqs.end()) return -PKA_ERR_SHAPE;
+    Request& r = it->second;
+    r.tokens.push_back(tokens[i]);
+    const int32_t need = m->blocks_for((int64_t)r.computed + 1) - (int32_t)r.blocks.size();
+    if (need > m->nfree) {
+      ok[i] = 0;
+      slots[i] = -1;
+      continue;
+    }
+    for (int32_t k = 0; k < need; ++k) r.blocks.push_back(m->pop_new());
+    const int32_t p = r.computed;
+    slots[i] = (int64_t)r.blocks[p / m->B] * m->B + p % m->B;
+    r.computed = p + 1;
+    m->register_filled(r);
+    ok[i] = 1;
+    ++done;
+  }
+  return done;
+}
+
 int32_t pka_bm_num_computed(const pka_block_manager* m, int64_t req_id) {
   if (!m) return -PKA_ERR_NULL;
   auto it = m->reqs.find(req_id);

@@ -128,3 +128,31 @@ def test_large_pool_throughput_sanity(pka):
     for rid in range(10000):
         m.free_request(rid)
     assert m.num_free() == 19035
+
+
+def test_batched_decode_step_matches_single_calls(pka):
+    """decode_step over many requests equals append_token + allocate(1) +
+    commit(1) request by request (reference), including a full pool."""
+    rng = random.Random(4)
+    N, B = 30, 4
+    cpp, ref = pka.BlockManager(N, B), RefBlockManager(N, B)
+    rids = list(range(1, 9))
+    for r in rids:
+        toks = [rng.randrange(20) for _ in range(rng.randrange(1, 10))]
+        cpp.add_request(r, toks)
+        ref.add_request(r, toks)
+        assert cpp.admit(r, len(toks)) == ref.admit(r, len(toks))
+        cpp.commit(r, len(toks) - cpp.computed(r))
+        ref.commit(r, len(toks) - ref.computed(r))
+    for step in range(12):
+        toks = [rng.randrange(20) for _ in rids]
+        slots, ok = cpp.decode_step(rids, toks)
+        for r, t, s, k in zip(rids, toks, slots.tolist(), ok.tolist()):
+            ref.append_token(r, t)
+            if ref.allocate(r, 1):
+                assert k and s == ref.slot_mapping(r, ref.computed(r), 1)[0]
+                ref.commit(r, 1)
+            else:
+                assert not k and s == -1
+        _same_state(cpp, ref, rids)
+    assert cpp.num_free() == 0  # the pool ran out on the way
