@@ -54,7 +54,7 @@ RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "8a05a50f968a9eee", 1189299152),
     "splitk": ("decode.hip", "8a05a50f968a9eee", 270924752),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
-    "mixed": ("prefill.hip", "4cce4cf0560dbad5", 45918208),
+    "mixed": ("prefill.hip", "19fd521fb9e96b52", 45902592),
 }
 
 
