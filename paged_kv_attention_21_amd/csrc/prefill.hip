@@ -284,20 +284,31 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int r = 0; r < PER; ++r)
     goff_bytes[r] = (uint32_t)((((my_row + r * ROWS_PER_PASS) % BS) * row_elems + (size_t)kvh * D + my_col) * 2);
-  auto fetch = [&](const uint16_t* __restrict__ cache, int tile, uint4 (&reg)[PER]) {
-    if (!mover) return;  // whole wavefronts (rows past the tile)
-    const int k0 = k_lo + tile * kPfKeys;
-    const int lb0 = k0 / BS;
+  // Byte offsets of the physical blocks that pass r of key tile `tile` reads
+  // (wavefront-uniform: scalar registers).  K tile t and V tile t use the same
+  // blocks, and V is fetched one step after K, so each tile's offsets are
+  // formed once and carried from the K fetch to the V fetch.
+  const uint32_t blk_bytes = (uint32_t)(blk_elems * 2);
+  auto block_offsets = [&](int tile, uint64_t (&off)[PER]) {
+    const int lb0 = (k_lo + tile * kPfKeys) / BS;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       // KV block of this pass inside the tile: the same for the whole
       // wavefront (its kWave / (D/8) rows never straddle a block boundary),
       // so it follows from the scalar wavefront index alone.
       const int blk_of = (wave * (kWave / (D / 8)) + r * ROWS_PER_PASS) / BS;
-      const int pb = tbl_row[min(lb0 + blk_of, lb_last)];
-      const uint16_t* base = cache + (size_t)pb * blk_elems;
+      const uint32_t pb = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
+      off[r] = (uint64_t)pb * blk_bytes;
+    }
+  };
+  auto fetch = [&](const uint16_t* __restrict__ cache, int tile, const uint64_t (&off)[PER], uint4 (&reg)[PER]) {
+    if (!mover) return;  // whole wavefronts (rows past the tile)
+    const int k0 = k_lo + tile * kPfKeys;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const char* base = reinterpret_cast<const char*>(cache) + off[r];
       const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, 0x7fffffff, kBufferFlags);
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff, kBufferFlags);
       reg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, goff_bytes[r], 0, 0));
     }
     if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
@@ -454,17 +465,23 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   floatx4_t s_a[NT][2], s_b[NT][2];
   uint4 pf[NT];
   const int last_tile = ntiles - 1;
+  uint64_t boff_a[PER], boff_b[PER];  // block offsets of two tiles
+  uint64_t boff_v[PER];               // offsets of the next V tile (from its K fetch)
   if (ntiles > 0) {
-    fetch(k_cache, 0, kreg_a);
-    fetch(v_cache, 0, vreg_a);
-    fetch(k_cache, min(1, last_tile), kreg_b);
+    block_offsets(0, boff_a);
+    block_offsets(min(1, last_tile), boff_b);
+    fetch(k_cache, 0, boff_a, kreg_a);
+    fetch(v_cache, 0, boff_a, vreg_a);
+    fetch(k_cache, min(1, last_tile), boff_b, kreg_b);
     stage(kbuf0, kreg_a);
     stage(vbuf0, vreg_a);
     stage(kbuf1, kreg_b);
-    fetch(k_cache, min(2, last_tile), kreg_a);
-    fetch(k_cache, min(3, last_tile), kreg_b);
-    fetch(v_cache, min(1, last_tile), vreg_b);
-    fetch(v_cache, min(2, last_tile), vreg_a);
+    fetch(v_cache, min(1, last_tile), boff_b, vreg_b);
+    block_offsets(min(2, last_tile), boff_a);
+    fetch(k_cache, min(2, last_tile), boff_a, kreg_a);
+    fetch(v_cache, min(2, last_tile), boff_a, vreg_a);
+    block_offsets(min(3, last_tile), boff_v);
+    fetch(k_cache, min(3, last_tile), boff_v, kreg_b);
     __syncthreads();
     qk(kbuf0, s_a);
     row_max(0, s_a);
@@ -484,8 +501,12 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t + 1 < ntiles) row_max(t + 1, snext);
     stage(kdst, kst);
     stage(vdst, vst);
-    fetch(k_cache, min(t + 4, last_tile), kst);
-    fetch(v_cache, min(t + 3, last_tile), vst);
+    uint64_t boff_k[PER];
+    block_offsets(min(t + 4, last_tile), boff_k);
+    fetch(k_cache, min(t + 4, last_tile), boff_k, kst);
+    fetch(v_cache, min(t + 3, last_tile), boff_v, vst);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) boff_v[r] = boff_k[r];
     __syncthreads();
   };
   for (int t = 0; t < ntiles; t += 2) {
