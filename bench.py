@@ -373,6 +373,36 @@ def bench_mixed(args, pka):
     flops = W.prefill_flops(step)
     tflops = flops / (pre_ms * 1e-3) / 1e12
     value = (dbytes + wbytes + pbytes) / (wall_ms * 1e-3) / 1e9
+    ceiling = None if args.no_arms else gemm_ceiling_tflops()
+
+    # Two-stream schedule of the same step (comparison arm): after the KV
+    # write, the HBM-bound decode runs on a second stream beside the
+    # MFMA-bound prefill (they write disjoint rows of `out`).
+    two_ms = None
+    if not args.no_arms:
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream(device=P.q.device)
+        with torch.cuda.stream(side):
+            decs2 = [pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws,
+                                           prepare=True) for r in range(P.R)]
+        written = torch.cuda.Event()
+        decoded = torch.cuda.Event()
+
+        def launch2(i, ev):
+            r = i % P.R
+            if ev:
+                ev[0].record(main)
+            writes[r]()
+            written.record(main)
+            side.wait_event(written)
+            decs2[r]()
+            pres[r]()
+            decoded.record(side)
+            main.wait_event(decoded)
+            if ev:
+                ev[1].record(main)
+
+        _, (two_ms,) = timed_loop(launch2, 1, args.steps, args.warmup)
     res = {
         "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
         "value": round(value, 2),
@@ -385,6 +415,8 @@ def bench_mixed(args, pka):
         "prefill_TFLOPs": round(tflops, 1),
         "unified_arm_us_per_call": None if args.no_arms else round(uni_ms * 1e3, 2),
         "unified_vs_split_attention": None if args.no_arms else round(uni_ms / (dec_ms + pre_ms), 2),
+        "two_stream_ms_per_step": None if two_ms is None else round(two_ms, 4),
+        "two_stream_GBps": None if two_ms is None else round((dbytes + wbytes + pbytes) / (two_ms * 1e-3) / 1e9, 2),
         "dtype": "bf16",
         "config": {
             "workload": "mixed paged step: KV write of 2048 rows, 64 decodes (ctx U[128,2048]) and ragged causal "
@@ -399,9 +431,31 @@ def bench_mixed(args, pka):
             "kernel": "paged_prefill_kernel", "bound": "mfma", "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
+            # What a plain library GEMM reaches on this GPU, beside the spec peak.
+            "measured_ceiling": ceiling,
+            "frac_of_measured_ceiling": None if ceiling is None else round(tflops / ceiling["TFLOPs"], 4),
         },
     }
     return res, step, True
+
+
+def gemm_ceiling_tflops(n=8192, reps=10):
+    """bf16 dense GEMM rate of the vendor library (torch.matmul -> hipBLASLt),
+    n x n x n, median of `reps` event-timed calls after warm-up."""
+    a = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0").to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        torch.matmul(a, b, out=c)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+    del a, b, c
+    return {"TFLOPs": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "gemm": f"bf16 {n}x{n}x{n} torch.matmul"}
 
 
 def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):

@@ -41,9 +41,9 @@
  * Arithmetic: fp32 accumulation; outputs rounded to nearest even.
  *
  * Supported shapes (mini_engine, "Roadmap": generalising beyond one head
- * shape): block_size 8, 16 or 32; head_dim 64, 128 or 256 (prefill: 64 or
- * 128); num_q_heads / num_kv_heads in {1, 2, 4, 8}; fp16 or bf16.  Anything
- * else returns PKA_ERR_UNSUPPORTED.
+ * shape): block_size 8, 16 or 32; head_dim 64, 128 or 256;
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; fp16 or bf16.  Anything else
+ * returns PKA_ERR_UNSUPPORTED.
  *
  * Errors: every host-checkable problem (null pointer, bad size, unsupported
  * shape, pointer not 16-byte aligned, workspace too small) returns a non-zero

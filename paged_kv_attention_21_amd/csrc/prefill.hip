@@ -84,26 +84,39 @@ struct Mfma<F16> {
 // staged K/V tile, so more wavefronts per tile means fewer K/V bytes pulled
 // through L2 per MFMA flop (the kernel is bound by that traffic at 4 waves).
 constexpr int kPfWaves = PKA_PREFILL_WAVES;
-constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRowsPerWave = 32;    // two 16-row MFMA tiles
-constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // q-rows per query tile (positions x group heads)
+constexpr int kPfThreads = kPfWaves * kWave;  // threads of the merge kernel (and of the attention kernel, D <= 128)
+constexpr int kPfRows = kPfWaves * 32;  // q-rows per query tile (positions x group heads)
+
+// Attention-kernel geometry by head size.  Up to 128 dims a wavefront owns 32
+// q-rows (two 16-row MFMA tiles); at 256 dims its output accumulators would
+// take 128 registers, so a wavefront owns 16 q-rows and the workgroup has
+// twice the wavefronts.  The query tile is kPfRows q-rows either way, which
+// keeps the split state and the merge independent of the head size.
+template <int D>
+struct PfGeom {
+  static constexpr int RPW = D == 256 ? 16 : 32;  // q-rows per wavefront
+  static constexpr int WAVES = kPfRows / RPW;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int NT = RPW / 16;             // 16-row MFMA tiles per wavefront
+  static_assert(THREADS <= 1024, "workgroup size");
+};
 constexpr int kPfKeys = 32;           // keys per staged tile (two KV blocks)
 // Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
 // swizzle, no stride).  Loads use offsets well inside num_records.
 constexpr int kBufferFlags = 0x00020000;
 constexpr float kPfSlack = 8.f;       // log2 growth of a row max tolerated before rescaling
 
-// LDS tiles.  Every row (of Q, K or V) takes 288 bytes whatever the head
-// size, and in K and V tiles the 16-byte pieces of rows 8..15 (mod 16) sit at
-// piece index XOR 8.  Measured on gfx950 (bank-conflict counters of single
+// LDS tiles.  Every row (of Q, K or V) takes 288 bytes up to 128 dims (544
+// bytes at 256: the same 32 bytes of padding), and in K and V tiles the
+// 16-byte pieces of rows 8..15 (mod 16) sit at piece index XOR 8.  Measured on gfx950 (bank-conflict counters of single
 // wavefronts), this is the layout where the three read patterns of the kernel
 // - K rows as the MFMA A operand, Q rows as the B operand, and the
 // transposing V reads - all run without bank conflicts; unpadded or
 // 16-byte-padded rows cost two to four extra cycles per read.
 template <int D>
 struct PfLds {
-  static_assert(D == 64 || D == 128, "pieces 0..15 after the swizzle");
-  static constexpr int ROW = 144;             // row stride in elements (288 bytes)
+  static_assert(D == 64 || D == 128 || D == 256, "supported head sizes");
+  static constexpr int ROW = D == 256 ? 272 : 144;  // row stride in elements
   static constexpr int TILE = kPfKeys * ROW;  // one [32 keys][D] tile
   static constexpr int STAGE = 2 * TILE;      // K tile, then V tile
 };
@@ -183,7 +196,7 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
 
 // BS = tokens per KV block (8, 16 or 32): a 32-key tile spans 32 / BS blocks.
 template <typename T, int D, int G, int BS>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(PfGeom<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
@@ -197,7 +210,9 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int BQ = kPfRows / G;     // query positions per tile
   constexpr int KSTEPS = D / 32;      // MFMA k-steps of QK^T
   constexpr int DTILES = D / 16;      // 16-dim tiles of the output
-  constexpr int NT = kPfRowsPerWave / 16;
+  constexpr int NT = PfGeom<D>::NT;
+  constexpr int RPW = PfGeom<D>::RPW;
+  constexpr int THREADS = PfGeom<D>::THREADS;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kPfRows * LD::ROW];  // the tile's q-rows
@@ -227,15 +242,15 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   int pos_of[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int pos = tl.q0 + (wave * kPfRowsPerWave + nt * 16 + l16) / G;
+    const int pos = tl.q0 + (wave * RPW + nt * 16 + l16) / G;
     pos_of[nt] = pos < tl.qlen ? pos : -1;
   }
-  constexpr int QPER = kPfRows * D / 8 / kPfThreads;  // 16-byte pieces of Q per thread
+  constexpr int QPER = kPfRows * D / 8 / THREADS;  // 16-byte pieces of Q per thread
   {
     uint4 qv[QPER];
 #pragma unroll
     for (int r = 0; r < QPER; ++r) {  // all loads first, then all LDS writes
-      const int c = threadIdx.x + r * kPfThreads;
+      const int c = threadIdx.x + r * THREADS;
       const int n = c / (D / 8), col = (c % (D / 8)) * 8;
       const int pos = tl.q0 + n / G;
       qv[r] = make_uint4(0, 0, 0, 0);
@@ -244,25 +259,26 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 #pragma unroll
     for (int r = 0; r < QPER; ++r) {
-      const int c = threadIdx.x + r * kPfThreads;
+      const int c = threadIdx.x + r * THREADS;
       *reinterpret_cast<uint4*>(q_lds + (c / (D / 8)) * LD::ROW + (c % (D / 8)) * 8) = qv[r];
     }
   }
   __syncthreads();  // q_lds
 
   // ---- global -> register -> LDS staging of one key tile ----
-  // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (256 / (D/8)),
-  // r < PER, for K and for V alike.  With D = 128 piece set r lies in KV block r;
-  // with D = 64 it lies in block (wave / 2): the block is wavefront-uniform,
-  // so its base address sits in scalar registers and each load adds a
-  // per-lane 32-bit offset.
+  // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (THREADS / (D/8)),
+  // r < PER, for K and for V alike.  A wavefront's 64 / (D/8) rows of one
+  // pass never straddle a KV block, so the block is wavefront-uniform: its
+  // base address sits in scalar registers and each load adds a per-lane
+  // 32-bit offset.
   constexpr int CHUNKS = kPfKeys * D / 8;             // 16-byte pieces per tile
   // With more threads than pieces (head size 64 at 8 wavefronts) the upper
   // threads move nothing.
-  constexpr int PER = CHUNKS >= kPfThreads ? CHUNKS / kPfThreads : 1;
-  static_assert(CHUNKS % kPfThreads == 0 || kPfThreads % CHUNKS == 0, "whole passes over the tile");
-  constexpr int ROWS_PER_PASS = kPfThreads / (D / 8);
-  const bool mover = CHUNKS >= kPfThreads || (int)threadIdx.x < CHUNKS;
+  constexpr int PER = CHUNKS >= THREADS ? CHUNKS / THREADS : 1;
+  static_assert(CHUNKS % THREADS == 0 || THREADS % CHUNKS == 0, "whole passes over the tile");
+  constexpr int ROWS_PER_PASS = THREADS / (D / 8);
+  static_assert(BS % (kWave / (D / 8)) == 0, "a wavefront's rows of one pass lie in one KV block");
+  const bool mover = CHUNKS >= THREADS || (int)threadIdx.x < CHUNKS;
   uint4 kreg_a[PER], kreg_b[PER], vreg_a[PER], vreg_b[PER];  // two prefetch sets per tensor
   const int my_row = threadIdx.x / (D / 8);           // row of pass 0
   const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
@@ -352,7 +368,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       uint4 qb[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        qb[nt] = *reinterpret_cast<const uint4*>(q_lds + (wave * kPfRowsPerWave + nt * 16 + l16) * LD::ROW +
+        qb[nt] = *reinterpret_cast<const uint4*>(q_lds + (wave * RPW + nt * 16 + l16) * LD::ROW +
                                                  32 * s + 8 * blk);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -434,14 +450,15 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // O^T += V^T P^T; the V^T operand (dims 16 dt + l16, keys 8 blk .. +7) comes
     // from the row-major V tile through two transposing reads.
     // Rows 8 blk + l16/4 (+4 for the upper half): swizzled when blk is odd,
-    // which moves dims 0..63 up by 64 elements and dims 64..127 down by 64.
+    // which moves each 128-dim group's dims 0..63 up by 64 elements and its
+    // dims 64..127 down by 64.
     const int vsw = (blk & 1) * 64;
     const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 4 * (l16 & 3);
-    const uint16_t* vlo = vrd + vsw;   // dim tiles 0..3
-    const uint16_t* vhi = vrd - vsw;   // dim tiles 4..7
+    const uint16_t* vlo = vrd + vsw;   // dim tiles 0..3 (mod 8)
+    const uint16_t* vhi = vrd - vsw;   // dim tiles 4..7 (mod 8)
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      const uint16_t* vp = (dt < 4 ? vlo : vhi) + 16 * dt;
+      const uint16_t* vp = ((dt & 4) ? vhi : vlo) + 16 * dt;
       const uint2 lo = lds_read_tr16(vp);
       const uint2 hi = lds_read_tr16(vp + 4 * LD::ROW);
       const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -518,7 +535,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = xor32_sum(xor16_sum(lpart[nt]));
-    const int n = wave * kPfRowsPerWave + nt * 16 + l16;
+    const int n = wave * RPW + nt * 16 + l16;
     if (tl.nsplit > 1) {
       // Unnormalised state of this split for the merge (invalid rows too: they are never stored).
       float* slot = partial + (((size_t)blockIdx.y * max_splits + split) * num_kv_heads + kvh) * pf_slot_floats(D);
@@ -639,7 +656,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int splits = (a.max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
   if (tiles > 65535 || splits > 65535) return hipErrorInvalidValue;
   dim3 grid(a.num_kv_heads, (unsigned)tiles, (unsigned)splits);
-  hipLaunchKernelGGL((paged_prefill_kernel<T, D, G, BS>), grid, dim3(kPfThreads), 0, stream, a.q, a.k_cache, a.v_cache,
+  hipLaunchKernelGGL((paged_prefill_kernel<T, D, G, BS>), grid, dim3(PfGeom<D>::THREADS), 0, stream, a.q, a.k_cache, a.v_cache,
                      a.block_tables, a.context_lens, a.query_start_loc, a.num_seqs, a.max_blocks_per_seq,
                      a.num_kv_heads, splits, a.scale * kLog2e, a.out, a.workspace);
   hipError_t e = hipGetLastError();
@@ -673,7 +690,7 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
 }
 
 bool prefill_supported(bool bf16, int head_dim, int group, int block_size) {
-  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8) &&
+  return (head_dim == 64 || head_dim == 128 || head_dim == 256) && (group == 1 || group == 2 || group == 4 || group == 8) &&
          (block_size == 8 || block_size == 16 || block_size == 32);
 }
 
@@ -681,9 +698,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.bf16) {
     if (a.head_dim == 64) return launch_prefill_g<BF16, 64>(a, stream);
     if (a.head_dim == 128) return launch_prefill_g<BF16, 128>(a, stream);
+    if (a.head_dim == 256) return launch_prefill_g<BF16, 256>(a, stream);
   } else {
     if (a.head_dim == 64) return launch_prefill_g<F16, 64>(a, stream);
     if (a.head_dim == 128) return launch_prefill_g<F16, 128>(a, stream);
+    if (a.head_dim == 256) return launch_prefill_g<F16, 256>(a, stream);
   }
   return hipErrorInvalidValue;
 }

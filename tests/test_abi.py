@@ -105,7 +105,7 @@ def test_prefill_validation(pka):
     assert pf(A, A, A, A, A, A, 2, 10, 5, 4, 16, 8, 0.1, A, d, None, 0, None) == 2     # max_context_len < max_query_len
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 12, 8, 0.1, A, d, None, 0, None) == 2   # 12 % 8
     bad = _desc(pka, bs=64, hkv=8, d=128, dt=1)
-    assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, _desc(pka, hkv=8, d=256, dt=1), None, 0, None) == 3
+    assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 128, 8, 0.1, A, d, None, 0, None) == 3    # GQA group 16
     assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, 0.1, A, bad, None, 0, None) == 3
     for scale in (0.0, -0.1, float("inf"), float("nan")):  # the running max assumes a positive scale
         assert pf(A, A, A, A, A, A, 2, 10, 5, 100, 16, 8, scale, A, d, None, 0, None) == 3

@@ -179,21 +179,25 @@ def test_prefill_repeat_and_placement_bit_identity(pka):
     assert torch.equal(a.cpu().view(torch.int16), c.cpu().view(torch.int16)), "block relabelling changed bits"
 
 
-# Block sizes 8 and 32 (a 32-key staging tile then spans four or one blocks).
+# Block sizes 8 and 32 (a 32-key staging tile then spans four or one blocks),
+# and head size 256 (eight wavefronts of 16 q-rows per query tile).
 GENERAL = [
     (torch.bfloat16, 16, 8, 128, 8),
     (torch.bfloat16, 16, 8, 128, 32),
     (torch.float16, 8, 2, 64, 8),
     (torch.float16, 8, 8, 64, 32),
+    (torch.bfloat16, 16, 8, 256, 16),
+    (torch.float16, 8, 4, 256, 32),
+    (torch.bfloat16, 8, 1, 256, 8),
 ]
 
 
 @pytest.mark.parametrize("shape", GENERAL, ids=[f"{str(s[0])[6:]}-{s[1]}q{s[2]}kv-d{s[3]}-b{s[4]}" for s in GENERAL])
-def test_general_block_sizes(pka, shape):
+def test_general_shapes(pka, shape):
     dtype, hq, hkv, d, bs = shape
     step = W.make_prefill_step(query_lens=[1, 31, 33, 64, 129, 200, 17], cached_lens=[0, 7, 1, 100, 40, 1100, 2047],
                                dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, seed=38,
                                poison=True, write_new=False)
     ds = DevStep(step)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step), dtype, f"prefill block size {shape}")
+    assert_parity(out, oracle_prefill(step), dtype, f"prefill shape {shape}")
