@@ -79,7 +79,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_step",
                    choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write",
-                            "block_manager"])
+                            "block_manager", "prefill_long"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate", type=int, default=0, help="pool copies to cycle (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
@@ -458,6 +458,83 @@ def gemm_ceiling_tflops(n=8192, reps=10):
     return {"TFLOPs": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "gemm": f"bf16 {n}x{n}x{n} torch.matmul"}
 
 
+def bench_prefill_long(args, pka):
+    """Prefill alone on long chunks: 4 sequences x 2,048 new rows after 6,144
+    cached tokens (bf16, 16q/8kv, head_dim 128), one launch (attention + split
+    merge).  MFMA-bound; the size where load balance no longer matters."""
+    ql, cached = [2048] * 4, [6144] * 4
+    step = W.make_prefill_step(query_lens=ql, cached_lens=cached, dtype=torch.bfloat16, num_q_heads=16,
+                               num_kv_heads=8, head_dim=128, seed=args.seed, poison=False, write_new=False)
+    dev = torch.device("cuda:0")
+    k, v, q = step.k_cache.to(dev), step.v_cache.to(dev), step.q.to(dev)
+    bt, cl, qsl = step.block_tables.to(dev), step.context_lens.to(dev), step.query_start_loc.to(dev)
+    out = torch.empty_like(q)
+    Hq, D, Hkv = q.shape[1], q.shape[2], step.num_kv_heads
+    mcl = int(step.context_lens.max())
+    ws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq, Hkv, D, mcl)),
+                     dtype=torch.uint8, device=dev)
+    run = pka.paged_attn_prefill(q, k, v, bt, cl, qsl, step.scale, step.max_query_len, mcl, out=out, workspace=ws,
+                                 prepare=True)
+
+    def launch(i, ev):
+        if ev:
+            ev[0].record()
+        run()
+        if ev:
+            ev[1].record()
+
+    wall_ms, (pre_ms,) = timed_loop(launch, 1, args.steps, args.warmup)
+    flops = W.prefill_flops(step)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    ceiling = None if args.no_arms else gemm_ceiling_tflops()
+    res = {
+        "metric": "paged prefill TFLOP/s (bf16 MFMA, algorithmic FLOPs), 1 MI355X",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(wall_ms, 4),
+        "prefill_us_per_call": round(pre_ms * 1e3, 2),
+        "dtype": "bf16",
+        "config": {"workload": "paged prefill: 4 chunks of 2,048 rows after 6,144 cached tokens each, bf16, "
+                               "16q/8kv, head_dim 128, block 16",
+                   "query_lens": ql, "cached_lens": cached, "seed": args.seed,
+                   "algorithmic": {"prefill_flops": flops, "prefill_bytes": W.prefill_bytes(step)}},
+        "roofline": {
+            "kernel": "paged_prefill_kernel", "bound": "mfma", "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "measured_ceiling": ceiling,
+            "frac_of_measured_ceiling": None if ceiling is None else round(tflops / ceiling["TFLOPs"], 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(step, args.cpu_seconds)
+    return res, None, False
+
+
+def cpu_baseline_prefill(step, budget_s):
+    """The oracle (as is) on a sample of the workload: rows of chunk 0 (each
+    sees the 6,144 cached keys plus its causal prefix), as many as the budget
+    allows, at least one; rate in algorithmic TFLOP/s."""
+    import oracle
+
+    threads = torch.get_num_threads()
+    Hq, D = step.q.shape[1], step.q.shape[2]
+    cached = int(step.context_lens[0]) - int(step.query_start_loc[1])
+    t0 = time.perf_counter()
+    rows = 0
+    flops = 0
+    while True:
+        oracle.prefill(step.q, step.k_cache, step.v_cache, step.block_tables, step.context_lens,
+                       step.query_start_loc, step.scale, seqs=[0], rows=[rows])
+        flops += 4 * D * Hq * (cached + rows + 1)
+        rows += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 torch-CPU oracle: the first {rows} rows of chunk 0 (6,144+ keys each) in {dt:.1f} s, "
+                      f"{threads} host threads"}
+
+
 def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
     rows = {}
     last = None
@@ -810,6 +887,8 @@ def main():
         res, step, write = bench_rope(args, pka)
     elif args.workload == "block_manager":
         res, step, write = bench_block_manager(args, pka)
+    elif args.workload == "prefill_long":
+        res, step, write = bench_prefill_long(args, pka)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
 

@@ -237,8 +237,11 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
  * weights are rounded to the input type before the PV product.
  *   query_start_loc  int32 [num_seqs + 1], query_start_loc[0] = 0,
  *                    query_start_loc[num_seqs] = num_q_tokens
- * Long chunks are split over several workgroups along the keys; their partial
- * states go to `workspace` (device memory, at least
+ * When the batch has too few query tiles (128 q-rows of one chunk and one KV
+ * head) to fill the GPU, each tile's key range is split over several
+ * workgroups (splits of at least 256 keys, enough of them for about four
+ * work items per compute unit); their partial states go to `workspace`
+ * (device memory, at least
  * pka_prefill_workspace_bytes(...) bytes, 256-byte aligned; contents need no
  * initialisation and are scratch after the call).  When that size is 0 the
  * workspace may be NULL.  PKA_ERR_WORKSPACE if it is needed and too small.
@@ -254,7 +257,9 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
                                void* stream);
 
 /* Workspace bytes pka_paged_attn_prefill needs for these sizes (0 when no
- * query tile can see more keys than one split holds).  Pure host function. */
+ * query tile can see more keys than one split holds).  Host function; the
+ * split choice uses the compute-unit count of the current device (256 when
+ * there is none), so size the workspace with the device the launch uses. */
 size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 

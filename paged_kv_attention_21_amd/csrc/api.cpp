@@ -313,8 +313,10 @@ size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32
   if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_context_len <= 0 || num_q_heads % num_kv_heads)
     return 0;
-  return pka::prefill_workspace_floats(num_q_tokens, num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
-                                       max_context_len) *
+  const int group = num_q_heads / num_kv_heads;
+  const int keys = pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, group, max_context_len,
+                                           pka_device_cu_count());
+  return pka::prefill_workspace_floats(num_q_tokens, num_seqs, num_kv_heads, group, head_dim, max_context_len, keys) *
          sizeof(float);
 }
 
@@ -363,6 +365,8 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   a.scale = scale;
   a.bf16 = cache.dtype == PKA_BF16;
   a.out = static_cast<uint16_t*>(out);
+  a.split_keys = pka::prefill_split_keys(num_q_tokens, num_seqs, cache.num_kv_heads, group, max_context_len,
+                                         pka_device_cu_count());
   a.workspace = need > 0 ? static_cast<float*>(workspace) : nullptr;
   return hip_status(pka::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }

@@ -11,10 +11,10 @@ constexpr int kPartitionSize = 256;
 
 // Keys per prefill split: a query tile that sees more keys is spread over
 // several workgroups whose states are merged afterwards.
-#ifndef PKA_PREFILL_SPLIT_KEYS
-#define PKA_PREFILL_SPLIT_KEYS 1024
-#endif
-constexpr int kPfSplitKeys = PKA_PREFILL_SPLIT_KEYS;
+// Shortest key range a prefill split is given (eight 32-key tiles), and the
+// split length held to in mixed batches (see prefill_split_keys).
+constexpr int kPfMinSplitKeys = 256;
+constexpr int kPfCapSplitKeys = 1024;
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -80,6 +80,7 @@ struct PrefillArgs {
   float scale;
   bool bf16;
   uint16_t* out;
+  int32_t split_keys;  // keys per split (multiple of 32), from prefill_split_keys
   float* workspace;  // split states; may be null when no tile needs more than one split
 };
 
@@ -103,7 +104,9 @@ hipError_t launch_rope_table(float* table, int max_position, int head_dim, doubl
 hipError_t launch_rope_kv_write(const RopeKvArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(bool bf16, int head_dim, int group, int block_size);
+int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int max_context_len,
+                       int num_cus);
 size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
-                                int max_context_len);
+                                int max_context_len, int split_keys);
 
 }  // namespace pka

@@ -11,7 +11,7 @@
 // Work items.  A query tile is 128 "q-rows" of one chunk and one KV head:
 // 128 / G query positions times the G query heads of the GQA group, so every
 // K/V tile staged in LDS serves all G heads.  The keys a query tile can see,
-// [0, kend), are cut into splits of kPfSplitKeys; one workgroup (4 wavefronts)
+// [0, kend), are cut into splits of split_keys; one workgroup (4 wavefronts)
 // takes one (KV head, query tile, split).  A tile with one split writes its
 // output directly; otherwise every split leaves its unnormalised state (row
 // max, exp-sum, O) in the workspace and a merge kernel combines them with the
@@ -21,15 +21,15 @@
 // same XCD (workgroups are dealt to the 8 XCDs round robin) and its K/V tiles
 // are shared through that XCD's L2.
 //
-// Inside a split the workgroup walks 32-key tiles (two KV blocks), staged in
-// LDS row-major (K and V alike) from registers loaded one tile ahead; the
-// split's block-table entries are staged in LDS first so no load waits on a
-// table read, and each tile's two block bases are wavefront-uniform (scalar
-// registers).  Each wavefront owns 32 q-rows (two 16-row MFMA tiles).
+// Inside a split the workgroup walks 32-key tiles, staged in LDS row-major
+// (K and V alike) from registers loaded two tiles ahead; a tile's physical
+// blocks come from scalar loads of the block table, so their base addresses
+// are wavefront-uniform (scalar registers).  Each wavefront owns 32 q-rows
+// (two 16-row MFMA tiles; 16 q-rows at head size 256).
 //
 // Products (v_mfma_f32_16x16x32, fp32 accumulate):
-//   S^T = K Q^T : A = 16 keys x 32 dims of K (LDS), B = Q^T fragment kept in
-//                 registers for the whole kernel.  The C layout then gives each
+//   S^T = K Q^T : A = 16 keys x 32 dims of K (LDS), B = Q^T fragment read from
+//                 the tile's q-rows, staged in LDS once.  The C layout then gives each
 //                 lane 4 keys of one q-row - exactly the lane's share of the
 //                 B operand of the next product, so the softmax weights never
 //                 leave registers.
@@ -44,6 +44,8 @@
 // masked keys selected out (-inf logit; K/V rows past the context are zeroed in
 // LDS so no NaN garbage reaches the products), fp32 accumulators, one
 // normalisation at the end, round to nearest even on store.
+
+#include <algorithm>
 
 #include "device_common.h"
 #include "launch.h"
@@ -178,7 +180,7 @@ struct PfTile {
 };
 
 __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
-                                        int num_seqs, int bq, int tile, PfTile* t) {
+                                        int num_seqs, int bq, int split_keys, int tile, PfTile* t) {
   int seq, qt;
   if (!find_tile(qsl, num_seqs, bq, tile, &seq, &qt)) return false;
   // Uniform across the wavefront: keep it (and all that follows) in scalar
@@ -190,7 +192,7 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
   t->cached = context_lens[t->seq] - t->qlen;
   t->q0 = t->qt * bq;
   t->kend = t->cached + t->q0 + min(bq, t->qlen - t->q0);  // keys [0, kend) are visible to some row
-  t->nsplit = (t->kend + kPfSplitKeys - 1) / kPfSplitKeys;
+  t->nsplit = (t->kend + split_keys - 1) / split_keys;
   return true;
 }
 
@@ -200,8 +202,8 @@ __global__ void __launch_bounds__(PfGeom<D>::THREADS) __attribute__((amdgpu_wave
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
-                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t max_splits,
-                     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ partial) {
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t split_keys,
+                     int32_t max_splits, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ partial) {
   using MM = Mfma<T>;
   using EL = Elem<T>;
   constexpr uint32_t kOnes2 = MM::kOne2;
@@ -220,7 +222,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int kvh = blockIdx.x;
   const int split = blockIdx.z;
   PfTile tl;
-  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, blockIdx.y, &tl)) return;
+  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, split_keys, blockIdx.y, &tl)) return;
   if (split >= tl.nsplit) return;  // this tile sees fewer keys
   if (tl.nsplit > max_splits) return;  // context longer than max_context_len: precondition broken
 
@@ -230,8 +232,8 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int blk = lane >> 4;
   const int num_q_heads = num_kv_heads * G;
   const int ctx = tl.cached + tl.qlen;
-  const int k_lo = split * kPfSplitKeys;
-  const int k_hi = min(tl.kend, k_lo + kPfSplitKeys);
+  const int k_lo = split * split_keys;
+  const int k_hi = min(tl.kend, k_lo + split_keys);
   const int ntiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
   const size_t row_elems = (size_t)num_kv_heads * D;
 
@@ -572,7 +574,7 @@ constexpr int kMgThreadsPerRow = kPfThreads / kMgRows;
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kPfThreads)
 paged_prefill_merge_kernel(const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
-                           int32_t num_seqs, int32_t num_kv_heads, int32_t max_splits,
+                           int32_t num_seqs, int32_t num_kv_heads, int32_t split_keys, int32_t max_splits,
                            const float* __restrict__ partial, uint16_t* __restrict__ out) {
   constexpr int BQ = kPfRows / G;
   constexpr int DPT = D / kMgThreadsPerRow;  // dims per thread
@@ -581,7 +583,7 @@ paged_prefill_merge_kernel(const int32_t* __restrict__ context_lens, const int32
   static_assert(DPT % 8 == 0, "whole 16-byte output pieces");
   const int kvh = blockIdx.x;
   PfTile tl;
-  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, blockIdx.y, &tl)) return;
+  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, split_keys, blockIdx.y, &tl)) return;
   if (tl.nsplit <= 1 || tl.nsplit > max_splits) return;
   const int n = blockIdx.z * kMgRows + threadIdx.x / kMgThreadsPerRow;  // q-row in the tile
   const int d0 = (threadIdx.x % kMgThreadsPerRow) * DPT;
@@ -643,9 +645,32 @@ size_t prefill_tiles_upper_bound(int num_q_tokens, int num_seqs, int group) {
   return (size_t)(num_q_tokens + bq - 1) / bq + num_seqs;
 }
 
+// Keys per split.  Splitting a query tile's key range buys parallelism at
+// the price of writing and merging a partial state per split, so it is used
+// only to fill the GPU: the number of (query tile, KV head) work items is
+// multiplied by the smallest split count that gives about four per compute
+// unit (two rounds of two resident workgroups), and no split is shorter than
+// kPfMinSplitKeys keys.  Batches with enough query tiles are not split at all.
+// The host sees only the longest context, not how the work spreads over the
+// chunks: when one long chunk shares a batch with short ones, its splits set
+// the critical path, so splits are held to kPfCapSplitKeys keys unless that
+// would more than double the work-item target (a batch of uniformly long
+// chunks, where longer splits cost less than the extra partial states).
+int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int max_context_len,
+                       int num_cus) {
+  const size_t items = prefill_tiles_upper_bound(num_q_tokens, num_seqs, group) * (size_t)num_kv_heads;
+  const size_t target = 4 * (size_t)(num_cus > 0 ? num_cus : 256);
+  size_t s = items >= target ? 1 : (target + items - 1) / items;
+  s = std::min(s, (size_t)std::max(1, (max_context_len + kPfMinSplitKeys - 1) / kPfMinSplitKeys));
+  int keys = (int)(((size_t)max_context_len + s - 1) / s);
+  const size_t capped_splits = ((size_t)max_context_len + kPfCapSplitKeys - 1) / kPfCapSplitKeys;
+  if (s > 1 && keys > kPfCapSplitKeys && items * capped_splits <= 2 * target) keys = kPfCapSplitKeys;
+  return std::max(kPfKeys, (keys + kPfKeys - 1) / kPfKeys * kPfKeys);
+}
+
 size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
-                                int max_context_len) {
-  const size_t splits = (size_t)(max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
+                                int max_context_len, int split_keys) {
+  const size_t splits = (size_t)(max_context_len + split_keys - 1) / split_keys;
   if (splits <= 1) return 0;
   return prefill_tiles_upper_bound(num_q_tokens, num_seqs, group) * splits * num_kv_heads * pf_slot_floats(head_dim);
 }
@@ -653,18 +678,19 @@ size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads
 template <typename T, int D, int G, int BS>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const size_t tiles = prefill_tiles_upper_bound(a.num_q_tokens, a.num_seqs, G);
-  const int splits = (a.max_context_len + kPfSplitKeys - 1) / kPfSplitKeys;
+  if (a.split_keys <= 0 || a.split_keys % kPfKeys) return hipErrorInvalidValue;
+  const int splits = (a.max_context_len + a.split_keys - 1) / a.split_keys;
   if (tiles > 65535 || splits > 65535) return hipErrorInvalidValue;
   dim3 grid(a.num_kv_heads, (unsigned)tiles, (unsigned)splits);
   hipLaunchKernelGGL((paged_prefill_kernel<T, D, G, BS>), grid, dim3(PfGeom<D>::THREADS), 0, stream, a.q, a.k_cache, a.v_cache,
                      a.block_tables, a.context_lens, a.query_start_loc, a.num_seqs, a.max_blocks_per_seq,
-                     a.num_kv_heads, splits, a.scale * kLog2e, a.out, a.workspace);
+                     a.num_kv_heads, a.split_keys, splits, a.scale * kLog2e, a.out, a.workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
   hipLaunchKernelGGL((paged_prefill_merge_kernel<T, D, G>), dim3(a.num_kv_heads, (unsigned)tiles, kPfRows / kMgRows),
                      dim3(kPfThreads),
-                     0, stream, a.context_lens, a.query_start_loc, a.num_seqs, a.num_kv_heads, splits, a.workspace,
-                     a.out);
+                     0, stream, a.context_lens, a.query_start_loc, a.num_seqs, a.num_kv_heads, a.split_keys, splits,
+                     a.workspace, a.out);
   return hipGetLastError();
 }
 

@@ -112,7 +112,40 @@ def test_prefill_validation(pka):
     # a tile can see more keys than one split holds: the workspace is required
     assert pf(A, A, A, A, A, A, 2, 10, 5, 5000, 16, 8, 0.1, A, d, None, 0, None) == 5
     need = pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 5000)
-    assert need > 0 and pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 1024) == 0
+    assert need > 0
+    # no split when every query tile fits in one split: a context no longer
+    # than the shortest split, or enough query tiles to fill the GPU
+    assert pka.prefill_workspace_bytes(2, 10, 16, 8, 128, 256) == 0
+    assert pka.prefill_workspace_bytes(4, 8192, 16, 8, 128, 8192) == 0
+
+
+def _prefill_splits(num_seqs, num_q_tokens, hkv, group, max_ctx, cus=256):
+    """The split count the library's policy gives (restated from its
+    definition: about four (query tile, KV head) items per compute unit,
+    splits of at least 256 keys and, in batches where that keeps the items
+    within twice the target, of at most 1,024; whole 32-key tiles)."""
+    tiles = -(-num_q_tokens // (128 // group)) + num_seqs
+    items = tiles * hkv
+    s = 1 if items >= 4 * cus else -(-4 * cus // items)
+    s = min(s, max(1, -(-max_ctx // 256)))
+    keys = -(-max_ctx // s)
+    if s > 1 and keys > 1024 and items * -(-max_ctx // 1024) <= 8 * cus:
+        keys = 1024
+    keys = max(32, -(-keys // 32) * 32)
+    return -(-max_ctx // keys), tiles
+
+
+@pytest.mark.parametrize("shape", [(2, 10, 8, 2, 5000), (5, 1984, 8, 2, 3072), (5, 1984, 8, 2, 5632),
+                                   (4, 2048, 8, 2, 16896),
+                                   (1, 7, 2, 1, 4096), (8, 4096, 8, 2, 8192), (3, 300, 4, 4, 700)])
+def test_prefill_split_policy(pka, shape):
+    """The workspace the library asks for is the split states of exactly the
+    split count the policy gives (CPU: the 256-CU default)."""
+    ns, nq, hkv, g, ctx = shape
+    d = 128
+    splits, tiles = _prefill_splits(ns, nq, hkv, g, ctx)
+    want = 0 if splits <= 1 else tiles * splits * hkv * 128 * (d + 2) * 4
+    assert pka.prefill_workspace_bytes(ns, nq, hkv * g, hkv, d, ctx) == want
 
 
 def test_workspace_bytes_and_dispatcher(pka):
