@@ -6,8 +6,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <climits>
 #include <cstdint>
 
 #include "launch.h"
@@ -72,6 +74,10 @@ int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, 
   a->head_dim = cache.head_dim;
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->block_size = cache.block_size;
+  // The single-pass kernel runs sequences longest first, bucketed against an
+  // upper bound of the context length (the table width unless the caller
+  // gives a tighter one).
+  a->order_max_ctx = (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * cache.block_size, INT32_MAX);
   a->scale = scale;
   a->bf16 = cache.dtype == PKA_BF16;
   return PKA_OK;
@@ -274,6 +280,7 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
   if (!aligned16(out)) return PKA_ERR_ALIGN;
   if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
   a.out = static_cast<uint16_t*>(out);
+  a.order_max_ctx = max_context_len;
   const int32_t cus = pka_device_cu_count();
   const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len, cus);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,6 +50,63 @@ struct DecodeLayout {
   static_assert(kWave % LPT == 0 && BS % TPL == 0 && kPartitionSize % BS == 0, "unsupported head_dim / block");
 };
 
+// Heavy-first order of the single-pass grid.  Workgroups start in grid order
+// as earlier ones finish, and a long sequence that starts last sets the
+// kernel's tail, so grid row r is given the r-th sequence in decreasing
+// order of context length - approximated by kOrderBuckets equal buckets of
+// [0, max_ctx], equal buckets in index order (longest-processing-time-first
+// list scheduling).  Every workgroup derives the same order from
+// context_lens: one load per sequence and thread group, a histogram in LDS
+// and one scan by the first wavefront.  Returns a wavefront-uniform index.
+constexpr int kOrderBuckets = kWave;  // one bucket per lane of the scan
+template <int NT>
+__device__ __forceinline__ int heavy_first_seq(const int32_t* __restrict__ context_lens, int num_seqs, int max_ctx,
+                                               int rank, int* lds /* kOrderBuckets + 1 ints */) {
+  const int tid = threadIdx.x;
+  auto bucket = [&](int i) {  // 0 holds the longest contexts
+    const long long c = max(context_lens[i], 0);
+    const int b = (int)(c * kOrderBuckets / ((long long)max_ctx + 1));
+    return kOrderBuckets - 1 - min(b, kOrderBuckets - 1);
+  };
+  if (tid < kOrderBuckets) lds[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < num_seqs; i += NT) atomicAdd(&lds[bucket(i)], 1);
+  __syncthreads();
+  if (tid < kWave) {
+    const int lane = tid;
+    const int cnt = lds[lane];
+    int incl = cnt;  // inclusive prefix sum over the buckets
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const int excl = incl - cnt;
+    const unsigned long long hit = __ballot(cnt > 0 && excl <= rank && rank < incl);
+    int found = rank;  // unreachable fallback: the given order
+    if (hit) {
+      const int k = __ffsll((long long)hit) - 1;  // the bucket holding position `rank`
+      int target = rank - __shfl(excl, k);
+      for (int base = 0; base < num_seqs; base += kWave) {
+        const int i = base + lane;
+        const bool match = i < num_seqs && bucket(i) == k;
+        const unsigned long long mask = __ballot(match);
+        const int n = __popcll(mask);
+        if (target < n) {
+          const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+          found = base + __ffsll((long long)__ballot(match && pos == target)) - 1;
+          break;
+        }
+        target -= n;
+      }
+    }
+    if (lane == 0) lds[kOrderBuckets] = found;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(lds[kOrderBuckets]);
+}
+
 // BS = tokens per KV block (8, 16 or 32).
 template <typename T, int D, int G, int W, bool SPLIT, int BS>
 __global__ void __launch_bounds__(W * kWave)
@@ -58,7 +115,7 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ context_lens, int32_t max_blocks_per_seq,
                     int32_t num_kv_heads, float scale_log2, uint16_t* __restrict__ out,
                     float* __restrict__ tmp_out, float* __restrict__ max_logits,
-                    float* __restrict__ exp_sums, int32_t max_num_partitions) {
+                    float* __restrict__ exp_sums, int32_t max_num_partitions, int32_t order_max_ctx) {
   using L = DecodeLayout<D, BS>;
   constexpr int kBlockSize = BS;
   using E = Elem<T>;
@@ -66,7 +123,11 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   const int kvh = blockIdx.x;
   const int part = SPLIT ? (int)blockIdx.y : 0;
-  const int seq = SPLIT ? (int)blockIdx.z : (int)blockIdx.y;
+  int seq = SPLIT ? (int)blockIdx.z : (int)blockIdx.y;
+  if constexpr (!SPLIT) {
+    __shared__ int order_lds[kOrderBuckets + 1];
+    if (order_max_ctx > 0) seq = heavy_first_seq<W * kWave>(context_lens, gridDim.y, order_max_ctx, seq, order_lds);
+  }
   const int num_q_heads = num_kv_heads * G;
 
   const int ctx = context_lens[seq];
@@ -370,6 +431,9 @@ constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per single-pass de
 #define PKA_SPLIT_WAVES 4
 #endif
 constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partition workgroup
+// Heavy-first ordering scans all context lengths in every workgroup; above
+// this many sequences the grid order is kept.
+constexpr int kOrderMaxSeqs = 1024;
 
 template <typename T, int D, int G, int BS>
 static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t stream) {
@@ -378,13 +442,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t s
     dim3 grid(a.num_kv_heads, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, false, BS>), grid, dim3(kDecodeWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
-                       a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0);
+                       a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0,
+                       a.num_seqs <= kOrderMaxSeqs ? a.order_max_ctx : 0);
   } else {
     dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true, BS>), grid, dim3(kSplitWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, nullptr, a.tmp_out, a.max_logits, a.exp_sums,
-                       a.max_num_partitions);
+                       a.max_num_partitions, 0);
   }
   return hipGetLastError();
 }

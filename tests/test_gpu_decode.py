@@ -117,6 +117,25 @@ def test_edge_context_lengths(pka, shape, variant):
     assert_parity(out, oracle_decode(step), dtype, f"edge lengths {shape} {variant}")
 
 
+@pytest.mark.parametrize("variant", ["v1", "auto"])
+@pytest.mark.parametrize("num_seqs", [600, 1100])
+def test_many_sequences_longest_first(pka, num_seqs, variant):
+    """The single pass runs sequences longest first (up to 1,024 sequences;
+    grid order above): every sequence must still be computed exactly once,
+    whatever its rank - lengths spread over many buckets, with ties, a few
+    very long contexts and some of one token."""
+    g = torch.Generator().manual_seed(num_seqs)
+    ctx = torch.randint(1, 200, (num_seqs,), generator=g)
+    ctx[torch.randint(0, num_seqs, (12,), generator=g)] = 1
+    ctx[torch.randint(0, num_seqs, (6,), generator=g)] = 1500
+    ctx[::97] = 64  # ties
+    step = W.make_decode_step(context_lens=ctx.tolist(), dtype=torch.float16, num_q_heads=4, num_kv_heads=2,
+                              head_dim=64, seed=num_seqs, poison=True)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant, max_ctx=int(ctx.max()))
+    assert_parity(out, oracle_decode(step), step.dtype, f"{num_seqs} sequences {variant}")
+
+
 def test_splitk_partition_state_matches_oracle(pka):
     step = W.make_decode_step(context_lens=[1, 255, 256, 257, 700, 2049], dtype=torch.bfloat16, num_q_heads=16,
                               num_kv_heads=8, head_dim=128, seed=8, poison=True)
