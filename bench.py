@@ -51,10 +51,11 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # (profiles/traffic_fetch_write.md), valid only for the kernel source they were
 # taken on: (source file, sha256 prefix, bytes).
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode.hip", "8a05a50f968a9eee", 1189299152),
-    "splitk": ("decode.hip", "8a05a50f968a9eee", 270924752),
+    "decode_step": ("decode.hip", "f978ae482d26593c", 1189330784),
+    "splitk": ("decode.hip", "f978ae482d26593c", 270950912),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
-    "mixed": ("prefill.hip", "19fd521fb9e96b52", 45902592),
+    "mixed": ("prefill.hip", "7fc2bc5f2a49d45f", 50156432),
+    "prefill_long": ("prefill.hip", "7fc2bc5f2a49d45f", 202053696),
 }
 
 
