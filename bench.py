@@ -128,10 +128,17 @@ class Pools:
         self.out = torch.empty_like(self.q)
 
 
-def timed_loop(launch, n_phases, steps, warmup):
+def percentiles(xs, qs=(10, 50, 90)):
+    """Nearest-rank percentiles of a list of timings."""
+    xs = sorted(xs)
+    return [xs[min(len(xs) - 1, max(0, math.ceil(q / 100 * len(xs)) - 1))] for q in qs]
+
+
+def timed_loop(launch, n_phases, steps, warmup, stats=None):
     """Run `launch(i, ev)` warmup + steps times; `ev` is a list of n_phases+1
     events the launcher records between its kernels.  Returns (wall ms per
-    step, per-phase mean ms from events)."""
+    step, per-phase mean ms from events); with `stats` (a dict), also stores
+    each phase's p10 / p50 / p90 in ms under stats["pct"]."""
     for i in range(warmup):
         launch(i, None)
     torch.cuda.synchronize()
@@ -142,8 +149,10 @@ def timed_loop(launch, n_phases, steps, warmup):
         launch(warmup + i, evs[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    phases = [sum(e[p].elapsed_time(e[p + 1]) for e in evs) / steps for p in range(n_phases)]
-    return wall_ms, phases
+    per = [[e[p].elapsed_time(e[p + 1]) for e in evs] for p in range(n_phases)]
+    if stats is not None:
+        stats["pct"] = [percentiles(x) for x in per]
+    return wall_ms, [sum(x) / steps for x in per]
 
 
 def graph_step_ms(capture_fns, steps, warmup):
@@ -221,7 +230,8 @@ def bench_decode_step(args, pka):
         if ev:
             ev[2].record()
 
-    wall_ms, (write_ms, dec_ms) = timed_loop(launch, 2, args.steps, args.warmup)
+    st = {}
+    wall_ms, (write_ms, dec_ms) = timed_loop(launch, 2, args.steps, args.warmup, stats=st)
     eager_ms = wall_ms
     graph_ms = None
     if not args.no_graph:
@@ -245,6 +255,7 @@ def bench_decode_step(args, pka):
         "step_launch": "hip-graph replay" if graph_ms is not None else "eager",
         "eager_ms_per_step": round(eager_ms, 4),
         "decode_us_per_call": round(dec_ms * 1e3, 2),
+        "decode_us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][1]],
         "kv_write_us_per_call": round(write_ms * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "dtype": "bf16",
@@ -556,7 +567,20 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
             if ev:
                 ev[1].record()
 
-        wall_ms, (dec_ms,) = timed_loop(launch, 1, args.steps, args.warmup)
+        st = {}
+        wall_ms, (dec_ms,) = timed_loop(launch, 1, args.steps, args.warmup, stats=st)
+        p10, p50, p90 = st["pct"][0]
+
+        # Cold: a 512 MiB write between calls pushes the pool out of the L2s
+        # and the Infinity Cache; the events bracket the decode alone.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+
+        def cold(i, ev):
+            flush.fill_(i & 0xFF)
+            launch(i, ev)
+
+        _, (cold_ms,) = timed_loop(cold, 1, args.steps, args.warmup)
+        del flush
 
         # Materialise-then-attend arm: gather the request's pages into
         # contiguous K/V, then plain torch attention (the pages' comparison
@@ -581,6 +605,8 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
         mwall, (gather_ms, sdpa_ms) = timed_loop(mat, 2, args.steps, args.warmup)
         rows[str(ctx)] = {
             "decode_us_per_call": round(dec_ms * 1e3, 2),
+            "decode_us_p10_p50_p90": [round(x * 1e3, 2) for x in (p10, p50, p90)],
+            "decode_cold_us_per_call": round(cold_ms * 1e3, 2),
             "decode_wall_us_per_call": round(wall_ms * 1e3, 2),
             "achieved_GBps": round(W.decode_bytes(step) / (dec_ms * 1e-3) / 1e9, 2),
             "materialise_then_attend_us": round(mwall * 1e3, 2),

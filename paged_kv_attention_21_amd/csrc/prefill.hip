@@ -21,15 +21,15 @@
 // same XCD (workgroups are dealt to the 8 XCDs round robin) and its K/V tiles
 // are shared through that XCD's L2.
 //
-// Inside a split the workgroup walks 32-key tiles, staged in LDS row-major
-// (K and V alike) from registers loaded two tiles ahead; a tile's physical
+// Inside a split the workgroup walks 64-key tiles, staged in LDS row-major
+// (K and V alike) from registers loaded one tile ahead; a tile's physical
 // blocks come from scalar loads of the block table, so their base addresses
 // are wavefront-uniform (scalar registers).  Each wavefront owns 32 q-rows
 // (two 16-row MFMA tiles; 16 q-rows at head size 256).
 //
 // Products (v_mfma_f32_16x16x32, fp32 accumulate):
-//   S^T = K Q^T : A = 16 keys x 32 dims of K (LDS), B = Q^T fragment read from
-//                 the tile's q-rows, staged in LDS once.  The C layout then gives each
+//   S^T = K Q^T : A = 16 keys x 32 dims of K (LDS), B = Q^T fragment kept in
+//                 registers for the whole split.  The C layout then gives each
 //                 lane 4 keys of one q-row - exactly the lane's share of the
 //                 B operand of the next product, so the softmax weights never
 //                 leave registers.
@@ -102,7 +102,7 @@ struct PfGeom {
   static constexpr int NT = RPW / 16;             // 16-row MFMA tiles per wavefront
   static_assert(THREADS <= 1024, "workgroup size");
 };
-constexpr int kPfKeys = 32;           // keys per staged tile (two KV blocks)
+constexpr int kPfKeys = 64;           // keys per staged tile (two 32-key halves)
 // Word 3 of a raw buffer descriptor (gfx9 family: 32-bit data format, no
 // swizzle, no stride).  Loads use offsets well inside num_records.
 constexpr int kBufferFlags = 0x00020000;
@@ -119,7 +119,7 @@ template <int D>
 struct PfLds {
   static_assert(D == 64 || D == 128 || D == 256, "supported head sizes");
   static constexpr int ROW = D == 256 ? 272 : 144;  // row stride in elements
-  static constexpr int TILE = kPfKeys * ROW;  // one [32 keys][D] tile
+  static constexpr int TILE = kPfKeys * ROW;  // one [64 keys][D] tile
   static constexpr int STAGE = 2 * TILE;      // K tile, then V tile
 };
 // Piece swizzle of K/V row `row`: 8 when bit 3 of the row is set.
@@ -196,7 +196,7 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
   return true;
 }
 
-// BS = tokens per KV block (8, 16 or 32): a 32-key tile spans 32 / BS blocks.
+// BS = tokens per KV block (8, 16 or 32): a 64-key tile spans 64 / BS blocks.
 template <typename T, int D, int G, int BS>
 __global__ void __launch_bounds__(PfGeom<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -215,9 +215,9 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int NT = PfGeom<D>::NT;
   constexpr int RPW = PfGeom<D>::RPW;
   constexpr int THREADS = PfGeom<D>::THREADS;
+  constexpr int KH = kPfKeys / 32;    // 32-key halves of a key tile
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kPfRows * LD::ROW];  // the tile's q-rows
 
   const int kvh = blockIdx.x;
   const int split = blockIdx.z;
@@ -237,35 +237,24 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int ntiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
   const size_t row_elems = (size_t)num_kv_heads * D;
 
-  // The tile's q-rows go to LDS once (row n = position n / G, head n % G of
-  // the group; rows past the chunk are zero); the Q^T B-operand fragments are
-  // read from there every key tile, which keeps 32 registers free for a
-  // second prefetch set.
+  // The Q^T B-operand fragments stay in registers for the whole split: lane
+  // (blk, l16) holds dims 32 s + 8 blk .. +7 of q-row l16 of row tile nt
+  // (q-row n = position n / G, head n % G of the group; rows past the chunk
+  // are zero).
   int pos_of[NT];
+  uint4 qf[KSTEPS][NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int pos = tl.q0 + (wave * RPW + nt * 16 + l16) / G;
+    const int n = wave * RPW + nt * 16 + l16;
+    const int pos = tl.q0 + n / G;
     pos_of[nt] = pos < tl.qlen ? pos : -1;
-  }
-  constexpr int QPER = kPfRows * D / 8 / THREADS;  // 16-byte pieces of Q per thread
-  {
-    uint4 qv[QPER];
+    const uint16_t* qrow = q + ((size_t)(tl.qstart + (pos < tl.qlen ? pos : 0)) * num_q_heads + kvh * G + n % G) * D;
 #pragma unroll
-    for (int r = 0; r < QPER; ++r) {  // all loads first, then all LDS writes
-      const int c = threadIdx.x + r * THREADS;
-      const int n = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int pos = tl.q0 + n / G;
-      qv[r] = make_uint4(0, 0, 0, 0);
-      if (pos < tl.qlen)
-        qv[r] = *reinterpret_cast<const uint4*>(q + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + col);
-    }
-#pragma unroll
-    for (int r = 0; r < QPER; ++r) {
-      const int c = threadIdx.x + r * THREADS;
-      *reinterpret_cast<uint4*>(q_lds + (c / (D / 8)) * LD::ROW + (c % (D / 8)) * 8) = qv[r];
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[s][nt] = make_uint4(0, 0, 0, 0);
+      if (pos < tl.qlen) qf[s][nt] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * blk);
     }
   }
-  __syncthreads();  // q_lds
 
   // ---- global -> register -> LDS staging of one key tile ----
   // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (THREADS / (D/8)),
@@ -274,14 +263,13 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // base address sits in scalar registers and each load adds a per-lane
   // 32-bit offset.
   constexpr int CHUNKS = kPfKeys * D / 8;             // 16-byte pieces per tile
-  // With more threads than pieces (head size 64 at 8 wavefronts) the upper
-  // threads move nothing.
+  // With more threads than pieces the upper threads move nothing.
   constexpr int PER = CHUNKS >= THREADS ? CHUNKS / THREADS : 1;
   static_assert(CHUNKS % THREADS == 0 || THREADS % CHUNKS == 0, "whole passes over the tile");
   constexpr int ROWS_PER_PASS = THREADS / (D / 8);
   static_assert(BS % (kWave / (D / 8)) == 0, "a wavefront's rows of one pass lie in one KV block");
   const bool mover = CHUNKS >= THREADS || (int)threadIdx.x < CHUNKS;
-  uint4 kreg_a[PER], kreg_b[PER], vreg_a[PER], vreg_b[PER];  // two prefetch sets per tensor
+  uint4 kreg[PER], vreg[PER];                         // the next tile, on its way to LDS
   const int my_row = threadIdx.x / (D / 8);           // row of pass 0
   const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
   const size_t blk_elems = (size_t)BS * row_elems;
@@ -289,11 +277,12 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // table entries inside the context are read): its rows are fetched from
   // memory the sequence owns and then zeroed.
 
-  // Rows of key tile `tile` of one cache (K or V) into registers.  The two
+  // Rows of key tile `tile` of one cache (K or V) into registers.  The
   // physical blocks come from the block table through scalar loads; each
   // block's base address goes into a buffer descriptor, so every lane's load
   // is the descriptor plus its own constant byte offset and no per-lane
-  // address arithmetic is left in the loop.
+  // address arithmetic is left in the loop.  K and V of one tile use the same
+  // blocks: the offsets are formed once per tile.
   const int32_t* __restrict__ tbl_row = block_tables + (size_t)tl.seq * max_blocks_per_seq;
   const int lb_last = (ctx - 1) / BS;  // last logical block inside the context
   // Byte offset of pass r's piece inside its block (the row's offset in the
@@ -302,46 +291,40 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int r = 0; r < PER; ++r)
     goff_bytes[r] = (uint32_t)((((my_row + r * ROWS_PER_PASS) % BS) * row_elems + (size_t)kvh * D + my_col) * 2);
-  // Byte offsets of the physical blocks that pass r of key tile `tile` reads
-  // (wavefront-uniform: scalar registers).  K tile t and V tile t use the same
-  // blocks, and V is fetched one step after K, so each tile's offsets are
-  // formed once and carried from the K fetch to the V fetch.
   const uint32_t blk_bytes = (uint32_t)(blk_elems * 2);
-  auto block_offsets = [&](int tile, uint64_t (&off)[PER]) {
-    const int lb0 = (k_lo + tile * kPfKeys) / BS;
+  auto fetch = [&](int tile) {
+    if (!mover) return;  // whole wavefronts (rows past the tile)
+    const int k0 = k_lo + tile * kPfKeys;
+    const int lb0 = k0 / BS;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       // KV block of this pass inside the tile: the same for the whole
-      // wavefront (its kWave / (D/8) rows never straddle a block boundary),
-      // so it follows from the scalar wavefront index alone.
+      // wavefront, so it follows from the scalar wavefront index alone.
       const int blk_of = (wave * (kWave / (D / 8)) + r * ROWS_PER_PASS) / BS;
       const uint32_t pb = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
-      off[r] = (uint64_t)pb * blk_bytes;
-    }
-  };
-  auto fetch = [&](const uint16_t* __restrict__ cache, int tile, const uint64_t (&off)[PER], uint4 (&reg)[PER]) {
-    if (!mover) return;  // whole wavefronts (rows past the tile)
-    const int k0 = k_lo + tile * kPfKeys;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const char* base = reinterpret_cast<const char*>(cache) + off[r];
-      const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, 0x7fffffff, kBufferFlags);
-      reg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, goff_bytes[r], 0, 0));
+      const uint64_t off = (uint64_t)pb * blk_bytes;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(k_cache) + off), (short)0, 0x7fffffff, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(v_cache) + off), (short)0, 0x7fffffff, kBufferFlags);
+      kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, goff_bytes[r], 0, 0));
+      vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, goff_bytes[r], 0, 0));
     }
     if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
       for (int r = 0; r < PER; ++r)
-        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) reg[r] = make_uint4(0, 0, 0, 0);
+        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) kreg[r] = vreg[r] = make_uint4(0, 0, 0, 0);
     }
   };
 
-  auto stage = [&](uint16_t* dst, const uint4 (&reg)[PER]) {
+  auto stage = [&](uint16_t* kdst, uint16_t* vdst) {
     if (!mover) return;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       const int row = my_row + r * ROWS_PER_PASS;
-      *reinterpret_cast<uint4*>(dst + row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3)) = reg[r];
+      const int at = row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3);
+      *reinterpret_cast<uint4*>(kdst + at) = kreg[r];
+      *reinterpret_cast<uint4*>(vdst + at) = vreg[r];
     }
   };
 
@@ -355,48 +338,42 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int dt = 0; dt < DTILES; ++dt) o[nt][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K row read by this lane in key half kt: key 8*(l16/4) + 4*kt + l16%4 of the
-  // tile; its pieces 4s + blk (< 8 for s < 2, >= 8 after) are swizzled by ksw.
+  // K row read by this lane in key quarter kt of a 32-key half: key
+  // 8*(l16/4) + 4*kt + l16%4 of the half; its pieces 4s + blk are swizzled by
+  // ksw (the half's base row is a multiple of 32, so the swizzle bit is that
+  // of the row inside the half).
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
-  const int ksw = pf_swz(krow0);  // 0 or 8, the same for both key halves
+  const int ksw = pf_swz(krow0);  // 0 or 8, the same for both key quarters
 
   auto qk = [&](const uint16_t* ks, floatx4_t (&sacc)[NT][2]) {
-    // S^T = K Q^T for both key halves and both q-row tiles; the Q^T fragments
-    // come from LDS one k-step at a time.
+    // S^T = K Q^T over one 32-key half and both q-row tiles.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sacc[nt][0] = sacc[nt][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      uint4 qb[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        qb[nt] = *reinterpret_cast<const uint4*>(q_lds + (wave * RPW + nt * 16 + l16) * LD::ROW +
-                                                 32 * s + 8 * blk);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const uint4 a = *reinterpret_cast<const uint4*>(ks + (krow0 + 4 * kt) * LD::ROW +
                                                         8 * ((4 * s + blk) ^ ksw));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = MM::mma(a, qb[nt], sacc[nt][kt]);
+        for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = MM::mma(a, qf[s][nt], sacc[nt][kt]);
       }
     }
-
   };
 
-  // Online softmax per q-row, in two parts; this lane holds keys 8*blk + 4*kt + i.
-  // The running max m is kept in raw score units (the scale is positive), so
-  // a weight is exp2(s * c - m * c) with c = scale * log2(e): one fma and one
-  // exp per score.
+  // Online softmax per q-row, one 32-key half at a time; this lane holds keys
+  // 8*blk + 4*kt + i of the half.  The running max m is kept in raw score
+  // units (the scale is positive), so a weight is exp2(s * c - m * c) with
+  // c = scale * log2(e): one fma and one exp per score.
   //
-  // Part 1: causal mask (only on tiles that reach the diagonal, a
+  // Part 1: causal mask (only on halves that reach the diagonal, a
   // wavefront-uniform test), row max, and the lazy rescale: the reference max
   // only moves when some row's max grows by more than kPfSlack in log2 units,
-  // so the accumulators are rescaled on a handful of tiles instead of on
+  // so the accumulators are rescaled on a handful of halves instead of on
   // every one; weights stay below 2^kPfSlack, harmless for fp32 sums and for
   // the (relative) bf16/fp16 rounding of P.
-  auto row_max = [&](int tile, floatx4_t (&sacc)[NT][2]) {
-    const int k0 = k_lo + tile * kPfKeys;
-    const bool diag = k0 + kPfKeys - 1 > tl.cached + tl.q0;
+  auto row_max = [&](int k0, floatx4_t (&sacc)[NT][2]) {
+    const bool diag = k0 + 31 > tl.cached + tl.q0;
     if (diag) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -414,7 +391,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const floatx4_t& s1 = sacc[nt][1];
       // This lane's max over its 8 keys; only when some lane exceeds the slack
       // is the full row max (over the row's four lanes) formed and the row
-      // rescaled, so the common tile needs no cross-lane traffic.
+      // rescaled, so the common half needs no cross-lane traffic.
       const float lmx = vmax(vmax3(vmax3(vmax3(s0[0], s0[1], s0[2]), s0[3], s1[0]), s1[1], s1[2]), s1[3]);
       if (__ballot(lmx > m[nt] + slack_raw)) {
         const float mx = xor32_max(xor16_max(lmx));
@@ -449,11 +426,11 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
 
   auto pv = [&](const uint16_t* vs, const uint4 (&pf)[NT]) {
-    // O^T += V^T P^T; the V^T operand (dims 16 dt + l16, keys 8 blk .. +7) comes
-    // from the row-major V tile through two transposing reads.
-    // Rows 8 blk + l16/4 (+4 for the upper half): swizzled when blk is odd,
-    // which moves each 128-dim group's dims 0..63 up by 64 elements and its
-    // dims 64..127 down by 64.
+    // O^T += V^T P^T over one 32-key half; the V^T operand (dims 16 dt + l16,
+    // keys 8 blk .. +7) comes from the row-major V tile through two
+    // transposing reads.  Rows 8 blk + l16/4 (+4 for the upper half):
+    // swizzled when blk is odd, which moves each 128-dim group's dims 0..63
+    // up by 64 elements and its dims 64..127 down by 64.
     const int vsw = (blk & 1) * 64;
     const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 4 * (l16 & 3);
     const uint16_t* vlo = vrd + vsw;   // dim tiles 0..3 (mod 8)
@@ -469,68 +446,41 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
 
-  // Software pipeline over key tiles, one barrier per tile.  K and V tiles
-  // have two LDS buffers each; while tile t's softmax runs, the MFMAs of
-  // S(t+1) = K(t+1) Q^T are already issued, so the matrix pipe and the VALU
-  // work on different tiles at once.  Step t reads K(t+1) and V(t), then
-  // stages K(t+2) over K(t) and V(t+1) over V(t-1), and fetches K(t+4) and
-  // V(t+3) into the registers just written out: every global load has two
-  // steps to land.  Fetch indices are clamped at the last tile, so the issue
-  // count is the same on every path and each wait stays exact.
-  uint16_t* const kbuf0 = lds;
-  uint16_t* const kbuf1 = lds + LD::TILE;
-  uint16_t* const vbuf0 = lds + 2 * LD::TILE;
-  uint16_t* const vbuf1 = lds + 3 * LD::TILE;
-  floatx4_t s_a[NT][2], s_b[NT][2];
-  uint4 pf[NT];
+  // Key tiles of 64 keys, double-buffered in LDS, one barrier per tile.  Step
+  // t computes on tile t (both halves) while tile t+1 - fetched into
+  // registers during step t-1 - is written to the other buffer and tile t+2
+  // is fetched: every global load has a whole step to land.  Within the step
+  // the two halves are interleaved so the softmax of one half can overlap
+  // the MFMAs of the other: S of both halves, then softmax + PV of half 0,
+  // then softmax + PV of half 1.  Fetch indices are clamped at the last tile,
+  // so every wave issues the same loads on every path and each wait stays
+  // exact.
   const int last_tile = ntiles - 1;
-  uint64_t boff_a[PER], boff_b[PER];  // block offsets of two tiles
-  uint64_t boff_v[PER];               // offsets of the next V tile (from its K fetch)
   if (ntiles > 0) {
-    block_offsets(0, boff_a);
-    block_offsets(min(1, last_tile), boff_b);
-    fetch(k_cache, 0, boff_a, kreg_a);
-    fetch(v_cache, 0, boff_a, vreg_a);
-    fetch(k_cache, min(1, last_tile), boff_b, kreg_b);
-    stage(kbuf0, kreg_a);
-    stage(vbuf0, vreg_a);
-    stage(kbuf1, kreg_b);
-    fetch(v_cache, min(1, last_tile), boff_b, vreg_b);
-    block_offsets(min(2, last_tile), boff_a);
-    fetch(k_cache, min(2, last_tile), boff_a, kreg_a);
-    fetch(v_cache, min(2, last_tile), boff_a, vreg_a);
-    block_offsets(min(3, last_tile), boff_v);
-    fetch(k_cache, min(3, last_tile), boff_v, kreg_b);
+    fetch(0);
+    stage(lds, lds + LD::TILE);
+    fetch(min(1, last_tile));
     __syncthreads();
-    qk(kbuf0, s_a);
-    row_max(0, s_a);
-    __syncthreads();  // K tile 0 is read by every wavefront before step 0 overwrites it
   }
-  auto step = [&](int t, floatx4_t (&scur)[NT][2], floatx4_t (&snext)[NT][2], const uint16_t* kread,
-                  const uint16_t* vread, uint16_t* kdst, uint16_t* vdst, uint4 (&kst)[PER], uint4 (&vst)[PER]) {
-    // S(t+1) (issued unconditionally: past the last tile it reads a stale
-    // buffer and is never used) and the weights of tile t have no dependence
-    // on each other, so the compiler may interleave the MFMAs with the VALU
-    // and exp work.
-    qk(kread, snext);
-    weights(scur, pf);
-    pv(vread, pf);
-    // Row max of tile t+1 (and the rare rescale, after PV(t) has added tile t
-    // at the old scale).
-    if (t + 1 < ntiles) row_max(t + 1, snext);
-    stage(kdst, kst);
-    stage(vdst, vst);
-    uint64_t boff_k[PER];
-    block_offsets(min(t + 4, last_tile), boff_k);
-    fetch(k_cache, min(t + 4, last_tile), boff_k, kst);
-    fetch(v_cache, min(t + 3, last_tile), boff_v, vst);
+  for (int t = 0; t < ntiles; ++t) {
+    const uint16_t* kt_lds = lds + (t & 1) * LD::STAGE;
+    const uint16_t* vt_lds = kt_lds + LD::TILE;
+    uint16_t* next = lds + ((t + 1) & 1) * LD::STAGE;
+    floatx4_t sh[KH][NT][2];
 #pragma unroll
-    for (int r = 0; r < PER; ++r) boff_v[r] = boff_k[r];
+    for (int h = 0; h < KH; ++h) qk(kt_lds + h * 32 * LD::ROW, sh[h]);
+    // Tile t+1 into the buffer tile t-1 used (free since the last barrier),
+    // then tile t+2 into the registers.
+    stage(next, next + LD::TILE);
+    fetch(min(t + 2, last_tile));
+#pragma unroll
+    for (int h = 0; h < KH; ++h) {
+      uint4 pf[NT];
+      row_max(k_lo + t * kPfKeys + 32 * h, sh[h]);
+      weights(sh[h], pf);
+      pv(vt_lds + h * 32 * LD::ROW, pf);
+    }
     __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, s_a, s_b, kbuf1, vbuf0, kbuf0, vbuf1, kreg_a, vreg_b);
-    if (t + 1 < ntiles) step(t + 1, s_b, s_a, kbuf0, vbuf1, kbuf1, vbuf0, kreg_b, vreg_a);
   }
 
   // Lane holds dims 16*dt + 4*blk + i of q-row l16 of tile nt.

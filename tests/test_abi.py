@@ -123,7 +123,7 @@ def _prefill_splits(num_seqs, num_q_tokens, hkv, group, max_ctx, cus=256):
     """The split count the library's policy gives (restated from its
     definition: about four (query tile, KV head) items per compute unit,
     splits of at least 256 keys and, in batches where that keeps the items
-    within twice the target, of at most 1,024; whole 32-key tiles)."""
+    within twice the target, of at most 1,024; whole 64-key tiles)."""
     tiles = -(-num_q_tokens // (128 // group)) + num_seqs
     items = tiles * hkv
     s = 1 if items >= 4 * cus else -(-4 * cus // items)
@@ -131,7 +131,7 @@ def _prefill_splits(num_seqs, num_q_tokens, hkv, group, max_ctx, cus=256):
     keys = -(-max_ctx // s)
     if s > 1 and keys > 1024 and items * -(-max_ctx // 1024) <= 8 * cus:
         keys = 1024
-    keys = max(32, -(-keys // 32) * 32)
+    keys = max(64, -(-keys // 64) * 64)
     return -(-max_ctx // keys), tiles
 
 
