@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_v1,
     paged_attn_prefill,
     paged_attn_splitk_reduce,
+    prefill_split_keys,
     prefill_workspace_bytes,
     rope_table,
     splitk_buffers,

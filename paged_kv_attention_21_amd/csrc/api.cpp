@@ -327,6 +327,15 @@ size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32
          sizeof(float);
 }
 
+int32_t pka_prefill_split_keys(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 ||
+      num_q_heads % num_kv_heads)
+    return -1;
+  return pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, num_q_heads / num_kv_heads, max_context_len,
+                                 pka_device_cu_count());
+}
+
 int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                const int32_t* context_lens, const int32_t* query_start_loc, int32_t num_seqs,
                                int32_t num_q_tokens, int32_t max_query_len, int32_t max_context_len,

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     for name in ("pka_kv_cache_write", "pka_paged_attn_decode", "pka_paged_attn_decode_v1",
                  "pka_paged_attn_decode_splitk", "pka_paged_attn_splitk_reduce", "pka_paged_attn_prefill",
                  "pka_splitk_workspace_bytes", "pka_decode_choose_variant", "pka_status_str",
-                 "pka_prefill_workspace_bytes", "pka_rope_table", "pka_rope_table_bytes", "pka_fused_rope_kv_write"):
+                 "pka_prefill_workspace_bytes", "pka_prefill_split_keys", "pka_rope_table", "pka_rope_table_bytes", "pka_fused_rope_kv_write"):
         assert name in syms
 
 
@@ -146,6 +146,8 @@ def test_prefill_split_policy(pka, shape):
     splits, tiles = _prefill_splits(ns, nq, hkv, g, ctx)
     want = 0 if splits <= 1 else tiles * splits * hkv * 128 * (d + 2) * 4
     assert pka.prefill_workspace_bytes(ns, nq, hkv * g, hkv, d, ctx) == want
+    keys = pka.prefill_split_keys(ns, nq, hkv * g, hkv, ctx)
+    assert keys % 64 == 0 and -(-ctx // keys) == splits
 
 
 def test_workspace_bytes_and_dispatcher(pka):

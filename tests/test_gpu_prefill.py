@@ -66,11 +66,20 @@ def test_ragged_chunks(pka, shape):
 @pytest.mark.parametrize("shape", [(torch.bfloat16, 16, 8, 128), (torch.float16, 8, 8, 64)],
                          ids=["bf16-16q8kv-d128", "fp16-8q8kv-d64"])
 def test_long_context_splits(pka, shape):
-    """Query tiles whose visible keys cross one or more key-split boundaries
-    (1,024 keys): exactly at a boundary, one past it, several splits, and a
-    single row after a 7,679-token prefix."""
+    """Query tiles whose visible keys cross key-split boundaries: a tile
+    ending exactly at the first boundary, one ending one key past it, one
+    ending exactly at the second, several splits, and a single row after a
+    7,679-token prefix (which fixes the longest context and so, with the
+    chunk sizes, the split length the launch picks)."""
     dtype, hq, hkv, d = shape
-    step = W.make_prefill_step(query_lens=[64, 65, 128, 1, 300, 17], cached_lens=[960, 960, 3000, 7679, 2500, 1023],
+    ql = [64, 65, 128, 1, 300, 17]
+    keys = pka.prefill_split_keys(len(ql), sum(ql), hq, hkv, 7680)
+    say(f"split length {keys} keys")
+    bq = 128 // (hq // hkv)  # query positions per tile
+    # first tile of chunk 0 ends at keys, of chunk 1 at keys + 1; chunk 5 ends at 2 * keys
+    cached = [keys - min(64, bq), keys + 1 - min(65, bq), 3000, 7679, 2500, 2 * keys - 17]
+    assert all(0 <= c and c + q <= 7680 for c, q in zip(cached, ql))
+    step = W.make_prefill_step(query_lens=ql, cached_lens=cached,
                                dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seed=36, poison=True,
                                write_new=False)
     ds = DevStep(step)
