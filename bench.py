@@ -194,6 +194,20 @@ def cpu_baseline_decode(step, write, budget_s):
             break
     per_pass = el / passes
     nbytes = W.decode_bytes(step) + (W.kv_write_bytes(step) if write else 0)
+    # The same oracle on one thread, on the first sequences for about a tenth
+    # of the budget, scaled by bytes.
+    torch.set_num_threads(1)
+    try:
+        n1 = 0
+        t1 = time.perf_counter()
+        while n1 < step.num_decode and time.perf_counter() - t1 < budget_s / 10:
+            n1 = min(step.num_decode, n1 + 8)
+            oracle.decode(step.decode_q, step.k_cache, step.v_cache, step.decode_block_tables,
+                          step.decode_context_lens, step.scale, seqs=list(range(n1 - 8, n1)))
+        el1 = time.perf_counter() - t1
+    finally:
+        torch.set_num_threads(threads)
+    one = W.decode_bytes(step, seqs=list(range(n1))) / el1 / 1e9
     return {
         "value": round(nbytes / per_pass / 1e9, 4),
         "unit": "GB/s",
@@ -201,9 +215,22 @@ def cpu_baseline_decode(step, write, budget_s):
         "kind": "oracle",
         "sample": f"fp64 torch-CPU oracle: {'KV write + ' if write else ''}decode of all {step.num_decode} "
                   f"sequences, {passes} pass(es) in {el:.1f} s ({per_pass * 1e3:.0f} ms/pass), "
-                  f"{os.cpu_count()} host CPUs visible",
+                  f"{os.cpu_count()} host CPUs visible ({cpu_model()})",
         "ms_per_step": round(per_pass * 1e3, 2),
+        "single_thread_value": round(one, 4),
+        "single_thread_sample": f"decode of the first {n1} sequences on 1 thread in {el1:.1f} s",
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "cpu model unknown"
 
 
 def bench_decode_step(args, pka):
