@@ -292,17 +292,25 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int r = 0; r < PER; ++r)
     goff_bytes[r] = (uint32_t)((((my_row + r * ROWS_PER_PASS) % BS) * row_elems + (size_t)kvh * D + my_col) * 2);
   const uint32_t blk_bytes = (uint32_t)(blk_elems * 2);
-  auto fetch = [&](int tile) {
-    if (!mover) return;  // whole wavefronts (rows past the tile)
-    const int k0 = k_lo + tile * kPfKeys;
-    const int lb0 = k0 / BS;
+  // Physical blocks of this wavefront's passes over key tile `tile` (scalar
+  // loads, issued a step before the fetch that uses them so their latency is
+  // hidden behind a whole tile of work).
+  auto lookup = [&](int tile, uint32_t (&pb)[PER]) {
+    const int lb0 = (k_lo + tile * kPfKeys) / BS;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       // KV block of this pass inside the tile: the same for the whole
       // wavefront, so it follows from the scalar wavefront index alone.
       const int blk_of = (wave * (kWave / (D / 8)) + r * ROWS_PER_PASS) / BS;
-      const uint32_t pb = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
-      const uint64_t off = (uint64_t)pb * blk_bytes;
+      pb[r] = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
+    }
+  };
+  auto fetch = [&](int tile, const uint32_t (&pb)[PER]) {
+    if (!mover) return;  // whole wavefronts (rows past the tile)
+    const int k0 = k_lo + tile * kPfKeys;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const uint64_t off = (uint64_t)pb[r] * blk_bytes;
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char*>(reinterpret_cast<const char*>(k_cache) + off), (short)0, 0x7fffffff, kBufferFlags);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -456,10 +464,15 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // so every wave issues the same loads on every path and each wait stays
   // exact.
   const int last_tile = ntiles - 1;
+  uint32_t pb_next[PER];  // blocks of the tile the next step fetches
   if (ntiles > 0) {
-    fetch(0);
+    uint32_t pb0[PER];
+    lookup(0, pb0);
+    lookup(min(1, last_tile), pb_next);
+    fetch(0, pb0);
     stage(lds, lds + LD::TILE);
-    fetch(min(1, last_tile));
+    fetch(min(1, last_tile), pb_next);
+    lookup(min(2, last_tile), pb_next);
     __syncthreads();
   }
   for (int t = 0; t < ntiles; ++t) {
@@ -472,7 +485,8 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // Tile t+1 into the buffer tile t-1 used (free since the last barrier),
     // then tile t+2 into the registers.
     stage(next, next + LD::TILE);
-    fetch(min(t + 2, last_tile));
+    fetch(min(t + 2, last_tile), pb_next);
+    lookup(min(t + 3, last_tile), pb_next);
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
       uint4 pf[NT];
