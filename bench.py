@@ -54,8 +54,8 @@ RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "f978ae482d26593c", 1189330784),
     "splitk": ("decode.hip", "f978ae482d26593c", 270950912),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
-    "mixed": ("prefill.hip", "7fc2bc5f2a49d45f", 50156432),
-    "prefill_long": ("prefill.hip", "7fc2bc5f2a49d45f", 202053696),
+    "mixed": ("prefill.hip", "cfa6ed1d392a2bf0", 50132168),
+    "prefill_long": ("prefill.hip", "cfa6ed1d392a2bf0", 201751712),
 }
 
 
