@@ -9,7 +9,8 @@
 // Work decomposition.  One workgroup per (KV head, sequence) - or per
 // (KV head, 256-token partition, sequence) for split-K.  The G query heads of
 // the GQA group ride along, so every K/V byte is loaded once and used G times.
-// The workgroup's W wavefronts take the range's KV blocks round-robin.
+// The workgroup's W wavefronts take the range's KV blocks round-robin.  The
+// single pass runs the sequences longest first (see heavy_first_seq).
 //
 // Lane layout inside a wavefront.  One 16-byte load per lane (8 elements)
 // makes a token row of D elements span LPT = D / 8 lanes, so one wave load

@@ -11,7 +11,7 @@ constexpr int kPartitionSize = 256;
 
 // Keys per prefill split: a query tile that sees more keys is spread over
 // several workgroups whose states are merged afterwards.
-// Shortest key range a prefill split is given (eight 32-key tiles), and the
+// Shortest key range a prefill split is given (four 64-key tiles), and the
 // split length held to in mixed batches (see prefill_split_keys).
 constexpr int kPfMinSplitKeys = 256;
 constexpr int kPfCapSplitKeys = 1024;
