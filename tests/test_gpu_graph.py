@@ -1,4 +1,5 @@
-"""HIP-graph capture of the decode step (KV write + dispatched decode): every
+"""HIP-graph capture of the decode step (KV write + dispatched decode) and of
+the mixed step (fused rotary write, decode, split prefill + merge): every
 replay, with eager work and synchronisations between replays, must reproduce
 the eager result bit for bit (output and pool)."""
 
@@ -48,6 +49,63 @@ def test_graph_replay_matches_eager(pka, ctx):
         run(out)
     for rep in range(3):
         out.fill_(float("nan"))
+        ds.k_cache.copy_(k0)
+        ds.v_cache.copy_(v0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"replay {rep}")
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep} output differs"
+        assert torch.equal(ds.k_cache.view(torch.int16), pool_k.view(torch.int16)), f"replay {rep} K pool differs"
+        assert torch.equal(ds.v_cache.view(torch.int16), pool_v.view(torch.int16)), f"replay {rep} V pool differs"
+
+
+def test_mixed_step_graph_replay_matches_eager(pka):
+    """The mixed step as the benchmark replays it: fused rotary + KV write of
+    the new rows, decode rows, and prefill chunks whose long prefix is split
+    (attention + merge kernels), captured once and replayed three times."""
+    step = W.make_mixed_step(decode_ctx=[40, 1300, 17, 700], query_lens=[37, 200, 64], cached_lens=[0, 2900, 128],
+                             sharing=[False] * 7, dtype=torch.bfloat16, num_q_heads=16, num_kv_heads=8,
+                             head_dim=128, seed=43, poison=True)
+    ds = DevStep(step)
+    nd = step.num_decode
+    S, Hq, D = step.q.shape
+    max_dec = int(step.decode_context_lens.max())
+    mcl = int(step.prefill_context_lens.max())
+    ws = torch.empty(max(1, pka.splitk_workspace_bytes(nd, Hq, D, max_dec)), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq,
+                                                         step.num_kv_heads, D, mcl)), dtype=torch.uint8,
+                      device="cuda")
+    assert pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq, step.num_kv_heads, D, mcl) > 0
+    table = pka.rope_table(4096, D, 1e6, "cuda")
+    qkv = W.fused_qkv(step).cuda()
+    pos = step.positions.cuda()
+    k0, v0 = ds.k_cache.clone(), ds.v_cache.clone()
+    q_rot = torch.empty_like(ds.q)
+
+    def run(out):
+        pka.fused_rope_kv_write(qkv, pos, ds.slot_mapping, table, Hq, ds.k_cache, ds.v_cache, q_out=q_rot)
+        pka.paged_attn_decode(q_rot[:nd], ds.k_cache, ds.v_cache, ds.block_tables[:nd], ds.context_lens[:nd],
+                              step.scale, max_dec, out=out[:nd], workspace=ws)
+        pka.paged_attn_prefill(q_rot[nd:], ds.k_cache, ds.v_cache, ds.block_tables[nd:], ds.context_lens[nd:],
+                               ds.query_start_loc, step.scale, step.max_query_len, mcl, out=out[nd:], workspace=pws)
+
+    say("graph capture of the mixed step")
+    eager = torch.empty_like(ds.q)
+    run(eager)
+    torch.cuda.synchronize()
+    assert torch.isfinite(eager.float()).all()
+    pool_k, pool_v = ds.k_cache.clone(), ds.v_cache.clone()
+    out = torch.empty_like(ds.q)
+    ds.k_cache.copy_(k0)
+    ds.v_cache.copy_(v0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        pws.fill_(0xFF)  # stale split states must not matter
         ds.k_cache.copy_(k0)
         ds.v_cache.copy_(v0)
         torch.cuda.synchronize()
