@@ -51,8 +51,8 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # (profiles/traffic_fetch_write.md), valid only for the kernel source they were
 # taken on: (source file, sha256 prefix, bytes).
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode.hip", "f978ae482d26593c", 1189330784),
-    "splitk": ("decode.hip", "f978ae482d26593c", 270950912),
+    "decode_step": ("decode.hip", "38cb238bfdad3000", 1189328960),
+    "splitk": ("decode.hip", "38cb238bfdad3000", 270950656),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
     "mixed": ("prefill.hip", "cfa6ed1d392a2bf0", 50132168),
     "prefill_long": ("prefill.hip", "cfa6ed1d392a2bf0", 201751712),
