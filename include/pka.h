@@ -226,6 +226,33 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode step with the KV-cache write folded in ([MS] "Engine" flowchart:
+ * the new token's K/V is written at slot = block_id * block_size + offset,
+ * then attention reads it; [ME] decode v1/v2).  For every sequence s with
+ * t = context_lens[s] - 1 >= 0:
+ *   the row key[s] / value[s] ([num_seqs][num_kv_heads][head_dim], the
+ *   cache dtype) is written, bit for bit, to position t of s, i.e. slot
+ *   block_tables[s][t / block_size] * block_size + t % block_size of
+ *   k_cache / v_cache,
+ *   and out[s] is the decode of pka_paged_attn_decode over positions
+ *   0 .. t, position t taking those rows.
+ * The result equals pka_kv_cache_write with slot_mapping[s] = that slot
+ * followed by pka_paged_attn_decode, in one launch (two with split-K); the
+ * kernels take the new rows from registers and never read the slot back, so
+ * its previous contents do not matter.  Same dispatch, workspace and errors
+ * as pka_paged_attn_decode; key, value: device pointers, 16-byte aligned
+ * (PKA_ERR_NULL / PKA_ERR_ALIGN).  Preconditions (unchecked): position t's
+ * block belongs to s alone (not a shared prefix block), and no other
+ * sequence of the batch has that slot.
+ */
+int32_t pka_paged_attn_decode_append(const void* q, const void* key, const void* value,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                                     void* out, pka_cache_desc cache, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Paged prefill ([ME] paged prefill attention; [MS] bottom-right causal
  * mask).  Ragged chunks packed in q: sequence s contributes rows
  * query_start_loc[s] .. query_start_loc[s+1]-1 (q_len_s rows) that occupy

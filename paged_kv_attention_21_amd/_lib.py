@@ -81,6 +81,11 @@ _SIGNATURES = {
         [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
          CacheDesc, c_void_p, c_size_t, c_void_p],
     ),
+    "pka_paged_attn_decode_append": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+         c_float, c_void_p, CacheDesc, c_void_p, c_size_t, c_void_p],
+    ),
     "pka_paged_attn_prefill": (
         c_int32,
         [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -474,6 +479,34 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ma
                     block_tables.shape[1], int(max_context_len), float(scale), _ptr(out), cache_desc(k_cache),
                     _ptr(workspace), ws_bytes, _stream(q)),
                    prepare, (q, k_cache, v_cache, block_tables, context_lens, out, workspace), out)
+
+
+def paged_attn_decode_append(q, key, value, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                             out=None, workspace=None, prepare=False):
+    """Decode step with the KV-cache write folded in: writes key[s] / value[s]
+    ([S, Hkv, D]) at position context_lens[s] - 1 of each sequence (the slot
+    its block table gives), then decodes over positions 0 .. context_lens[s] - 1
+    - the same result as kv_cache_write followed by paged_attn_decode.
+    Arguments otherwise as paged_attn_decode."""
+    _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    S, Hq, D = q.shape
+    for t, name in ((key, "key"), (value, "value")):
+        _require(t, name, dtype=k_cache.dtype, ndim=3, device=q.device)
+        if tuple(t.shape) != (S, k_cache.shape[2], D):
+            raise ValueError(f"{name} must be [{S}, {k_cache.shape[2]}, {D}], got {tuple(t.shape)}")
+    out = _out_like(q, out)
+    need = splitk_workspace_bytes(S, Hq, D, max_context_len)
+    if workspace is None and decode_choose_variant(S, k_cache.shape[2], max_context_len) == 2:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+        ws_bytes = workspace.numel()
+    return _launch(lib.pka_paged_attn_decode_append,
+                   (_ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                    _ptr(context_lens), S, Hq, block_tables.shape[1], int(max_context_len), float(scale), _ptr(out),
+                    cache_desc(k_cache), _ptr(workspace), ws_bytes, _stream(q)),
+                   prepare, (q, key, value, k_cache, v_cache, block_tables, context_lens, out, workspace), out)
 
 
 def prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:

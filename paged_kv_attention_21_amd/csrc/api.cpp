@@ -83,6 +83,66 @@ int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, 
   return PKA_OK;
 }
 
+// Dispatched decode (single pass, or split-K + reduce); new_k / new_v non-null
+// append one token per sequence (pka_paged_attn_decode_append).
+int32_t decode_dispatch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* out,
+                        const pka_cache_desc& cache, void* workspace, size_t workspace_bytes, void* stream,
+                        const void* new_k, const void* new_v) {
+  if (num_seqs < 0 || max_context_len < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  if (max_context_len == 0) return PKA_ERR_SHAPE;
+  pka::DecodeArgs a;
+  int32_t st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                              max_blocks_per_seq, scale, cache, &a);
+  if (st) return st;
+  if (!out) return PKA_ERR_NULL;
+  if (!aligned16(out)) return PKA_ERR_ALIGN;
+  if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
+  a.out = static_cast<uint16_t*>(out);
+  a.order_max_ctx = max_context_len;
+  if (new_k) {
+    a.new_k = static_cast<const uint16_t*>(new_k);
+    a.new_v = static_cast<const uint16_t*>(new_v);
+    a.k_store = static_cast<uint16_t*>(const_cast<void*>(k_cache));
+    a.v_store = static_cast<uint16_t*>(const_cast<void*>(v_cache));
+  }
+  const int32_t cus = pka_device_cu_count();
+  const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len, cus);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (variant == 1) return hip_status(pka::launch_decode(a, false, s));
+
+  const int32_t P = num_partitions(max_context_len);
+  if (P > 65535) return PKA_ERR_UNSUPPORTED;
+  const size_t need = pka_splitk_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len);
+  if (!workspace || workspace_bytes < need) return PKA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKA_ERR_ALIGN;
+  const size_t rows = (size_t)num_seqs * num_q_heads * P;
+  char* w = static_cast<char*>(workspace);
+  a.max_num_partitions = P;
+  a.tmp_out = reinterpret_cast<float*>(w);
+  a.max_logits = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)));
+  a.exp_sums = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)) +
+                                        align256(rows * sizeof(float)));
+  hipError_t e = pka::launch_decode(a, true, s);
+  if (e != hipSuccess) return PKA_ERR_HIP;
+  pka::ReduceArgs r{};
+  r.tmp_out = a.tmp_out;
+  r.max_logits = a.max_logits;
+  r.exp_sums = a.exp_sums;
+  r.context_lens = context_lens;
+  r.num_seqs = num_seqs;
+  r.num_q_heads = num_q_heads;
+  r.head_dim = cache.head_dim;
+  r.partition_size = pka::kPartitionSize;
+  r.max_num_partitions = P;
+  r.bf16 = a.bf16;
+  r.out = a.out;
+  return hip_status(pka::launch_splitk_reduce(r, s));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -269,50 +329,19 @@ int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                               int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* out,
                               pka_cache_desc cache, void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || max_context_len < 0) return PKA_ERR_SHAPE;
-  if (num_seqs == 0) return PKA_OK;
-  if (max_context_len == 0) return PKA_ERR_SHAPE;
-  pka::DecodeArgs a;
-  int32_t st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
-                              max_blocks_per_seq, scale, cache, &a);
-  if (st) return st;
-  if (!out) return PKA_ERR_NULL;
-  if (!aligned16(out)) return PKA_ERR_ALIGN;
-  if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
-  a.out = static_cast<uint16_t*>(out);
-  a.order_max_ctx = max_context_len;
-  const int32_t cus = pka_device_cu_count();
-  const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len, cus);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (variant == 1) return hip_status(pka::launch_decode(a, false, s));
+  return decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                         max_context_len, scale, out, cache, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
 
-  const int32_t P = num_partitions(max_context_len);
-  if (P > 65535) return PKA_ERR_UNSUPPORTED;
-  const size_t need = pka_splitk_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len);
-  if (!workspace || workspace_bytes < need) return PKA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKA_ERR_ALIGN;
-  const size_t rows = (size_t)num_seqs * num_q_heads * P;
-  char* w = static_cast<char*>(workspace);
-  a.max_num_partitions = P;
-  a.tmp_out = reinterpret_cast<float*>(w);
-  a.max_logits = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)));
-  a.exp_sums = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)) +
-                                        align256(rows * sizeof(float)));
-  hipError_t e = pka::launch_decode(a, true, s);
-  if (e != hipSuccess) return PKA_ERR_HIP;
-  pka::ReduceArgs r{};
-  r.tmp_out = a.tmp_out;
-  r.max_logits = a.max_logits;
-  r.exp_sums = a.exp_sums;
-  r.context_lens = context_lens;
-  r.num_seqs = num_seqs;
-  r.num_q_heads = num_q_heads;
-  r.head_dim = cache.head_dim;
-  r.partition_size = pka::kPartitionSize;
-  r.max_num_partitions = P;
-  r.bf16 = a.bf16;
-  r.out = a.out;
-  return hip_status(pka::launch_splitk_reduce(r, s));
+int32_t pka_paged_attn_decode_append(const void* q, const void* key, const void* value, void* k_cache,
+                                     void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                     int32_t max_context_len, float scale, void* out, pka_cache_desc cache,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!key || !value)) return PKA_ERR_NULL;
+  if (num_seqs > 0 && (!aligned16(key) || !aligned16(value))) return PKA_ERR_ALIGN;
+  return decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                         max_context_len, scale, out, cache, workspace, workspace_bytes, stream, key, value);
 }
 
 size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,

@@ -116,7 +116,9 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const int32_t* __restrict__ context_lens, int32_t max_blocks_per_seq,
                     int32_t num_kv_heads, float scale_log2, uint16_t* __restrict__ out,
                     float* __restrict__ tmp_out, float* __restrict__ max_logits,
-                    float* __restrict__ exp_sums, int32_t max_num_partitions, int32_t order_max_ctx) {
+                    float* __restrict__ exp_sums, int32_t max_num_partitions, int32_t order_max_ctx,
+                    const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v,
+                    uint16_t* __restrict__ k_store, uint16_t* __restrict__ v_store) {
   using L = DecodeLayout<D, BS>;
   constexpr int kBlockSize = BS;
   using E = Elem<T>;
@@ -146,6 +148,21 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int wave = wave_id();
   const int row = lane / LPT;
   const int col = lane % LPT;  // this lane's 8 dims: col*8 .. col*8+7
+
+  // Appended token (when new_k is given): position ctx - 1 of every sequence
+  // is the row new_k / new_v [seq][kvh] - the decode step's KV-cache write
+  // folded into the attention that reads it.  The wavefront that consumes
+  // the range's last block takes that position's K/V from registers (the
+  // cached copy may be stale or NaN until then: it is loaded and selected
+  // out, never read back) and stores the row to its slot, whose block it
+  // already holds, so no extra table lookup delays the start of the loop.
+  const bool append = new_k != nullptr && ctx > 0 && tok_end == ctx;
+  uint4 app_k = make_uint4(0, 0, 0, 0), app_v = app_k;
+  if (append) {
+    const size_t src = ((size_t)seq * num_kv_heads + kvh) * D + col * 8;
+    app_k = *reinterpret_cast<const uint4*>(new_k + src);
+    app_v = *reinterpret_cast<const uint4*>(new_v + src);
+  }
 
   // q pieces of the G heads of this group.
   uint32_t qv[G][4];
@@ -242,11 +259,34 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  auto consume = [&](const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int blk) {
-    if (blk == nblk - 1 && last_valid < kBlockSize)
+  // pb: the block's physical id (used only for the appended token's store).
+  auto consume = [&](const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int blk, int pb) {
+    if (blk == nblk - 1 && append) {
+      // The range's last block holds the appended token at row last_valid - 1:
+      // load i = (last_valid - 1) / TPL, lane row (last_valid - 1) % TPL.
+      uint4 ka2[LPB], va2[LPB];
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        const bool mine = i * TPL + row == last_valid - 1;
+        ka2[i] = mine ? app_k : kk[i];
+        va2[i] = mine ? app_v : vv[i];
+      }
+      if (row == (last_valid - 1) % TPL) {
+        const uint32_t off = lane_off[0] + (uint32_t)(((last_valid - 1) / TPL) * TPL * row_elems * 2);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
+                                  off) = app_k;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
+                                  off) = app_v;
+      }
+      if (last_valid < kBlockSize)
+        consume_t(std::true_type{}, ka2, va2, last_valid);
+      else
+        consume_t(std::false_type{}, ka2, va2, kBlockSize);
+    } else if (blk == nblk - 1 && last_valid < kBlockSize) {
       consume_t(std::true_type{}, kk, vv, last_valid);
-    else
+    } else {
       consume_t(std::false_type{}, kk, vv, kBlockSize);
+    }
   };
 
   // Main loop, double-buffered over this wavefront's blocks: while a block is
@@ -264,16 +304,16 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
     int j = 0;
     for (; j + 3 < jn; j += 2) {
-      consume(ka, va, blk_base + j * W);
+      consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
       issue(uniform_lane(tbl_win, j + 2), ka, va);
-      consume(kb2, vb2, blk_base + (j + 1) * W);
+      consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
       issue(uniform_lane(tbl_win, j + 3), kb2, vb2);
     }
     const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
-    consume(ka, va, blk_base + j * W);
+    consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
     if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
-    if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * W);
-    if (rem == 3) consume(ka, va, blk_base + (j + 2) * W);
+    if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
+    if (rem == 3) consume(ka, va, blk_base + (j + 2) * W, uniform_lane(tbl_win, j + 2));
   }
 
   // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
@@ -444,13 +484,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t s
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, false, BS>), grid, dim3(kDecodeWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0,
-                       a.num_seqs <= kOrderMaxSeqs ? a.order_max_ctx : 0);
+                       a.num_seqs <= kOrderMaxSeqs ? a.order_max_ctx : 0, a.new_k, a.new_v, a.k_store, a.v_store);
   } else {
     dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true, BS>), grid, dim3(kSplitWaves * kWave), 0,
                        stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                        a.num_kv_heads, scale_log2, nullptr, a.tmp_out, a.max_logits, a.exp_sums,
-                       a.max_num_partitions, 0);
+                       a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store);
   }
   return hipGetLastError();
 }

@@ -36,6 +36,12 @@ struct DecodeArgs {
   float* tmp_out;    // split-K only
   float* max_logits;
   float* exp_sums;
+  // Appended token (pka_paged_attn_decode_append): rows [num_seqs][kv heads][D]
+  // stored at position context_lens[s] - 1 and attended from registers; null otherwise.
+  const uint16_t* new_k;
+  const uint16_t* new_v;
+  uint16_t* k_store;  // the caches again, writable
+  uint16_t* v_store;
 };
 
 struct ReduceArgs {

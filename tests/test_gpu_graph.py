@@ -1,4 +1,5 @@
-"""HIP-graph capture of the decode step (KV write + dispatched decode) and of
+"""HIP-graph capture of the decode step (KV write + dispatched decode, as two
+launches and with the write folded into the decode launch) and of
 the mixed step (fused rotary write, decode, split prefill + merge): every
 replay, with eager work and synchronisations between replays, must reproduce
 the eager result bit for bit (output and pool)."""
@@ -19,8 +20,9 @@ def pka():
     return pka
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["write+decode", "decode_append"])
 @pytest.mark.parametrize("ctx", [[300, 1500, 77, 2000], [4000, 9000]], ids=["single-pass", "split-k"])
-def test_graph_replay_matches_eager(pka, ctx):
+def test_graph_replay_matches_eager(pka, ctx, fused):
     step = W.make_decode_step(context_lens=ctx, dtype=torch.bfloat16, num_q_heads=16, num_kv_heads=8, head_dim=128,
                               seed=41, poison=True, write_new=True)
     ds = DevStep(step)
@@ -30,11 +32,15 @@ def test_graph_replay_matches_eager(pka, ctx):
     k0, v0 = ds.k_cache.clone(), ds.v_cache.clone()
 
     def run(out):
+        if fused:
+            pka.paged_attn_decode_append(ds.q, ds.new_k, ds.new_v, ds.k_cache, ds.v_cache, ds.block_tables,
+                                         ds.context_lens, step.scale, max_ctx, out=out, workspace=ws)
+            return
         pka.kv_cache_write(ds.new_k, ds.new_v, ds.slot_mapping, ds.k_cache, ds.v_cache)
         pka.paged_attn_decode(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.context_lens, step.scale, max_ctx,
                               out=out, workspace=ws)
 
-    say(f"graph capture of the decode step, ctx={ctx}")
+    say(f"graph capture of the decode step, ctx={ctx}, fused={fused}")
     eager = torch.empty_like(ds.q)
     run(eager)
     torch.cuda.synchronize()
