@@ -54,8 +54,8 @@ RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "b0eafdfbd3e2dfaa", 1191570899),
     "splitk": ("decode.hip", "b0eafdfbd3e2dfaa", 271005696),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
-    "mixed": ("prefill.hip", "cfa6ed1d392a2bf0", 50132168),
-    "prefill_long": ("prefill.hip", "cfa6ed1d392a2bf0", 201751712),
+    "mixed": ("prefill.hip", "9e580416d01ccc87", 50132800),
+    "prefill_long": ("prefill.hip", "9e580416d01ccc87", 201632992),
 }
 
 
