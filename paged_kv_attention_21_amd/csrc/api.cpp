@@ -80,6 +80,7 @@ int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, 
   a->order_max_ctx = (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * cache.block_size, INT32_MAX);
   a->scale = scale;
   a->bf16 = cache.dtype == PKA_BF16;
+  a->num_cus = std::max<int32_t>(0, pka_device_cu_count());
   return PKA_OK;
 }
 

@@ -30,6 +30,7 @@ struct DecodeArgs {
   int32_t block_size;          // tokens per KV block: 8, 16 or 32
   int32_t max_num_partitions;  // split-K only
   int32_t order_max_ctx;       // single pass: > 0 runs sequences longest first (bucketed by this bound)
+  int32_t num_cus;             // compute units of the device (0 if unknown)
   float scale;
   bool bf16;
   uint16_t* out;     // single pass only

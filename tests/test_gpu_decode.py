@@ -238,3 +238,22 @@ def test_general_block_and_head_sizes(pka, shape, variant):
     assert torch.equal(ds.v_cache.cpu().view(torch.int16), vc.view(torch.int16)), "KV write not bit-exact"
     out = run_decode(pka, ds, variant)
     assert_parity(out, oracle_decode(step, k_cache=kc, v_cache=vc), dtype, f"general {shape} {variant}")
+
+
+@pytest.mark.parametrize("num_seqs,hkv", [(40, 8), (64, 8), (150, 2), (33, 8)])
+def test_one_round_grid_pairing(pka, num_seqs, hkv):
+    """Grids of more (sequence, KV head) workgroups than compute units but at
+    most two per unit reverse the order of the rows that take a second slot
+    (long sequences paired with short ones): every sequence must still be
+    computed exactly once, whatever its rank."""
+    cus = pka.device_cu_count()
+    say(f"one-round pairing: {num_seqs} seqs x {hkv} KV heads on {cus} CUs")
+    g = torch.Generator().manual_seed(num_seqs * hkv)
+    ctx = torch.randint(1, 2049, (num_seqs,), generator=g)
+    ctx[::7] = 1
+    step = W.make_decode_step(context_lens=ctx.tolist(), dtype=torch.bfloat16, num_q_heads=2 * hkv, num_kv_heads=hkv,
+                              head_dim=128, seed=num_seqs, poison=True)
+    ds = DevStep(step)
+    for variant in ("v1", "auto"):
+        out = run_decode(pka, ds, variant)
+        assert_parity(out, oracle_decode(step), step.dtype, f"pairing {num_seqs}x{hkv} {variant}")
