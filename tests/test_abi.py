@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     for name in ("pka_kv_cache_write", "pka_paged_attn_decode", "pka_paged_attn_decode_v1",
                  "pka_paged_attn_decode_splitk", "pka_paged_attn_splitk_reduce", "pka_paged_attn_prefill",
                  "pka_splitk_workspace_bytes", "pka_decode_choose_variant", "pka_status_str",
-                 "pka_prefill_workspace_bytes", "pka_prefill_split_keys", "pka_rope_table", "pka_rope_table_bytes", "pka_fused_rope_kv_write"):
+                 "pka_prefill_workspace_bytes", "pka_prefill_split_keys", "pka_rope_table", "pka_rope_table_bytes", "pka_fused_rope_kv_write",
+                 "pka_paged_attn_decode_append"):
         assert name in syms
 
 
@@ -93,6 +94,13 @@ def test_decode_validation(pka):
     auto = lib.pka_paged_attn_decode
     assert auto(A, A, A, A, A, 1, 2, 8, 0, 0.125, A, d, None, 0, None) == 2  # max_context_len 0
     assert auto(A, A, A, None, A, 1, 2, 8, 128, 0.125, A, d, None, 0, None) == 1
+    app = lib.pka_paged_attn_decode_append
+    assert app(A, A, A, A, A, A, A, 0, 2, 8, 128, 0.125, A, d, None, 0, None) == 0      # no sequences: no-op
+    assert app(A, None, A, A, A, A, A, 1, 2, 8, 128, 0.125, A, d, None, 0, None) == 1   # no new K rows
+    assert app(A, A, None, A, A, A, A, 1, 2, 8, 128, 0.125, A, d, None, 0, None) == 1   # no new V rows
+    assert app(A, A + 2, A, A, A, A, A, 1, 2, 8, 128, 0.125, A, d, None, 0, None) == 4  # misaligned rows
+    assert app(A, A, A, A, A, None, A, 1, 2, 8, 128, 0.125, A, d, None, 0, None) == 1   # no block tables
+    assert app(A, A, A, A, A, A, A, 1, 2, 8, 0, 0.125, A, d, None, 0, None) == 2        # max_context_len 0
 
 
 def test_prefill_validation(pka):

@@ -210,3 +210,33 @@ def test_general_shapes(pka, shape):
     ds = DevStep(step)
     out = run_prefill(pka, ds)
     assert_parity(out, oracle_prefill(step), dtype, f"prefill shape {shape}")
+
+
+def test_long_prefill_bench_size_sampled_rows(pka):
+    """The long-prefill workload at the size and in the launch configuration
+    the benchmark times (4 chunks of 2,048 rows after 6,144 cached tokens,
+    bf16, 16q/8kv, head_dim 128, workspace sized by the library), checked on
+    sampled rows: both ends of every chunk, rows around query-tile (64
+    positions) boundaries, and random rows."""
+    ql, cached = [2048] * 4, [6144] * 4
+    step = W.make_prefill_step(query_lens=ql, cached_lens=cached, dtype=torch.bfloat16, num_q_heads=16,
+                               num_kv_heads=8, head_dim=128, seed=0, poison=True, write_new=False)
+    ds = DevStep(step)
+    Hq, D, Hkv = step.num_q_heads, step.head_dim, step.num_kv_heads
+    mcl = int(step.prefill_context_lens.max())
+    ws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq, Hkv, D, mcl)),
+                     dtype=torch.uint8, device="cuda")
+    say(f"long prefill at bench size: split length {pka.prefill_split_keys(4, 8192, Hq, Hkv, mcl)} keys")
+    out = pka.paged_attn_prefill(ds.prefill_q, ds.k_cache, ds.v_cache, ds.prefill_block_tables,
+                                 ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len, mcl,
+                                 out=None, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(5)
+    rows = set()
+    for j in range(4):
+        b = j * 2048
+        rows.update(b + r for r in (0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2046, 2047))
+        rows.update((b + torch.randint(0, 2048, (6,), generator=g)).tolist())
+    rows = sorted(rows)
+    ref = oracle_prefill(step, rows=rows)
+    assert_parity(out.cpu()[rows], ref[rows], step.dtype, f"long prefill bench size, {len(rows)} sampled rows")
