@@ -227,9 +227,9 @@ def cpu_baseline_decode(step, write, budget_s):
         n1 = 0
         t1 = time.perf_counter()
         while n1 < step.num_decode and time.perf_counter() - t1 < budget_s / 10:
-            n1 = min(step.num_decode, n1 + 8)
+            n0, n1 = n1, min(step.num_decode, n1 + 8)
             oracle.decode(step.decode_q, step.k_cache, step.v_cache, step.decode_block_tables,
-                          step.decode_context_lens, step.scale, seqs=list(range(n1 - 8, n1)))
+                          step.decode_context_lens, step.scale, seqs=list(range(n0, n1)))
         el1 = time.perf_counter() - t1
     finally:
         torch.set_num_threads(threads)
