@@ -53,7 +53,7 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "c629906f18649f21", 1191575008),
     "splitk": ("decode.hip", "c629906f18649f21", 271019816),
-    "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908416),
+    "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908832),
     "mixed": ("prefill.hip", "9e580416d01ccc87", 50132800),
     "prefill_long": ("prefill.hip", "9e580416d01ccc87", 201632992),
 }
