@@ -462,7 +462,7 @@ def bench_mixed(args, pka):
     _, (write_ms, dec_ms, pre_ms, uni_ms) = timed_loop(launch, 4, args.steps, args.warmup)
     eager_ms = write_ms + dec_ms + pre_ms
     wall_ms = eager_ms
-    graph_ms = None
+    graph_ms = graph2_ms = None
     if not args.no_graph:
         # The step as a captured HIP graph (write, decode, prefill + merge),
         # one per pool copy, replayed in turn.
@@ -474,6 +474,24 @@ def bench_mixed(args, pka):
                                                    workspace=pws))
         graph_ms = graph_step_ms([step_fn(r) for r in range(P.R)], args.steps, args.warmup)
         wall_ms = graph_ms
+
+        # Comparison arm: the same step with the HBM-bound decode forked onto a
+        # second stream beside the MFMA-bound prefill (they write disjoint rows
+        # of `out`), joined before the step ends, captured into one graph.
+        side_g = torch.cuda.Stream(device=P.q.device)  # default priority
+
+        def step_fn2(r):
+            def fn():
+                pka.kv_cache_write(P.new_k, P.new_v, P.slots, P.k[r], P.v[r])
+                side_g.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side_g):
+                    pka.paged_attn_decode(qd, P.k[r], P.v[r], btd, cld, step.scale, max_dec, out=od, workspace=ws)
+                pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql, mcl, out=op,
+                                       workspace=pws)
+                torch.cuda.current_stream().wait_stream(side_g)
+            return fn
+        # Comparison arm only: measured slower as a graph than the one-stream step.
+        graph2_ms = graph_step_ms([step_fn2(r) for r in range(P.R)], args.steps, args.warmup)
     dbytes = W.decode_bytes(step)
     wbytes = W.kv_write_bytes(step)
     pbytes = W.prefill_bytes(step)
@@ -516,6 +534,8 @@ def bench_mixed(args, pka):
         "unit": "GB/s",
         "ms_per_step": round(wall_ms, 4),
         "step_launch": "hip-graph replay" if graph_ms is not None else "eager (event sum)",
+        "graph_ms_per_step_one_stream": None if graph_ms is None else round(graph_ms, 4),
+        "graph_ms_per_step_two_streams": None if graph_ms is None else round(graph2_ms, 4),
         "eager_ms_per_step": round(eager_ms, 4),
         "kv_write_us_per_call": round(write_ms * 1e3, 2),
         "decode_us_per_call": round(dec_ms * 1e3, 2),

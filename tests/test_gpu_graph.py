@@ -66,7 +66,8 @@ def test_graph_replay_matches_eager(pka, ctx, fused):
         assert torch.equal(ds.v_cache.view(torch.int16), pool_v.view(torch.int16)), f"replay {rep} V pool differs"
 
 
-def test_mixed_step_graph_replay_matches_eager(pka):
+@pytest.mark.parametrize("two_streams", [False, True], ids=["one-stream", "decode-on-side-stream"])
+def test_mixed_step_graph_replay_matches_eager(pka, two_streams):
     """The mixed step as the benchmark replays it: fused rotary + KV write of
     the new rows, decode rows, and prefill chunks whose long prefix is split
     (attention + merge kernels), captured once and replayed three times."""
@@ -89,14 +90,25 @@ def test_mixed_step_graph_replay_matches_eager(pka):
     k0, v0 = ds.k_cache.clone(), ds.v_cache.clone()
     q_rot = torch.empty_like(ds.q)
 
+    side = torch.cuda.Stream()  # default priority
+
     def run(out):
         pka.fused_rope_kv_write(qkv, pos, ds.slot_mapping, table, Hq, ds.k_cache, ds.v_cache, q_out=q_rot)
-        pka.paged_attn_decode(q_rot[:nd], ds.k_cache, ds.v_cache, ds.block_tables[:nd], ds.context_lens[:nd],
-                              step.scale, max_dec, out=out[:nd], workspace=ws)
+        if two_streams:
+            # Fork: the decode rows on a side stream beside the prefill; join before the end.
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                pka.paged_attn_decode(q_rot[:nd], ds.k_cache, ds.v_cache, ds.block_tables[:nd], ds.context_lens[:nd],
+                                      step.scale, max_dec, out=out[:nd], workspace=ws)
+        else:
+            pka.paged_attn_decode(q_rot[:nd], ds.k_cache, ds.v_cache, ds.block_tables[:nd], ds.context_lens[:nd],
+                                  step.scale, max_dec, out=out[:nd], workspace=ws)
         pka.paged_attn_prefill(q_rot[nd:], ds.k_cache, ds.v_cache, ds.block_tables[nd:], ds.context_lens[nd:],
                                ds.query_start_loc, step.scale, step.max_query_len, mcl, out=out[nd:], workspace=pws)
+        if two_streams:
+            torch.cuda.current_stream().wait_stream(side)
 
-    say("graph capture of the mixed step")
+    say(f"graph capture of the mixed step, two streams: {two_streams}")
     eager = torch.empty_like(ds.q)
     run(eager)
     torch.cuda.synchronize()
