@@ -491,7 +491,8 @@ def bench_mixed(args, pka):
                 torch.cuda.current_stream().wait_stream(side_g)
             return fn
         # Comparison arm only: measured slower as a graph than the one-stream step.
-        graph2_ms = graph_step_ms([step_fn2(r) for r in range(P.R)], args.steps, args.warmup)
+        if not args.no_arms:
+            graph2_ms = graph_step_ms([step_fn2(r) for r in range(P.R)], args.steps, args.warmup)
     dbytes = W.decode_bytes(step)
     wbytes = W.kv_write_bytes(step)
     pbytes = W.prefill_bytes(step)
@@ -535,7 +536,7 @@ def bench_mixed(args, pka):
         "ms_per_step": round(wall_ms, 4),
         "step_launch": "hip-graph replay" if graph_ms is not None else "eager (event sum)",
         "graph_ms_per_step_one_stream": None if graph_ms is None else round(graph_ms, 4),
-        "graph_ms_per_step_two_streams": None if graph_ms is None else round(graph2_ms, 4),
+        "graph_ms_per_step_two_streams": None if graph2_ms is None else round(graph2_ms, 4),
         "eager_ms_per_step": round(eager_ms, 4),
         "kv_write_us_per_call": round(write_ms * 1e3, 2),
         "decode_us_per_call": round(dec_ms * 1e3, 2),
