@@ -54,8 +54,8 @@ RECORDED_TRAFFIC = {
     "decode_step": ("decode.hip", "c629906f18649f21", 1191575008),
     "splitk": ("decode.hip", "c629906f18649f21", 271019816),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908832),
-    "mixed": ("prefill.hip", "9e580416d01ccc87", 50132800),
-    "prefill_long": ("prefill.hip", "9e580416d01ccc87", 201632992),
+    "mixed": ("prefill.hip", "26823a696a320f6b", 50132520),
+    "prefill_long": ("prefill.hip", "26823a696a320f6b", 201633088),
 }
 
 
