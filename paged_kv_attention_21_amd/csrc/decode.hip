@@ -382,11 +382,13 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
 }
 
-// Split-K reduce: one workgroup per (query head, sequence).  Partitions are
-// taken in passes of up to kReduceChunk: the threads find the pass's max
-// logit and weights w_p = l_p exp(m_p - M) in parallel (weights kept in LDS),
-// then thread t accumulates dim t % D over partitions t / D, t / D + GROUPS, ...
-// with independent loads in flight; a running max rescales earlier passes.
+// Split-K reduce: one workgroup per (query head, sequence, chunk of
+// ReduceGeom::DC dims).  Partitions are taken in passes of up to kReduceChunk:
+// the threads find the pass's max logit and weights w_p = l_p exp(m_p - M) in
+// parallel (weights kept in LDS; every dim chunk recomputes them, a few loads
+// per partition), then thread t accumulates dim t % DC of the chunk over
+// partitions t / DC, t / DC + GROUPS, ... with independent loads in flight; a
+// running max rescales earlier passes.
 constexpr int kReduceThreads = 256;
 constexpr int kReduceChunk = 1024;
 
@@ -406,20 +408,34 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* scrat
   return v;
 }
 
+// Dims per reduce workgroup: the head's dims are spread over D / kReduceDims
+// workgroups, so a few (sequence, head) pairs still fill the GPU and each
+// thread walks a quarter of the partitions it would otherwise.
+#ifndef PKA_REDUCE_DIMS
+#define PKA_REDUCE_DIMS 32
+#endif
+template <int D>
+struct ReduceGeom {
+  static constexpr int DC = D < PKA_REDUCE_DIMS ? D : PKA_REDUCE_DIMS;  // dims per workgroup
+  static constexpr int CHUNKS = D / DC;
+};
+
 template <typename T, int D>
 __global__ void __launch_bounds__(kReduceThreads)
 splitk_reduce_kernel(const float* __restrict__ tmp_out, const float* __restrict__ max_logits,
                      const float* __restrict__ exp_sums, const int32_t* __restrict__ context_lens,
                      int32_t num_q_heads, int32_t partition_size, int32_t max_num_partitions,
                      uint16_t* __restrict__ out) {
-  constexpr int GROUPS = kReduceThreads / D;
+  constexpr int DC = ReduceGeom<D>::DC;
+  constexpr int GROUPS = kReduceThreads / DC;
   __shared__ float s_w[kReduceChunk];
   __shared__ float s_red[kReduceThreads / kWave];
-  __shared__ float s_acc[GROUPS][D];
+  __shared__ float s_acc[GROUPS][DC];
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int t = threadIdx.x;
-  const int d = t % D, grp = t / D;
+  const int dl = t % DC, grp = t / DC;
+  const int d = blockIdx.z * DC + dl;  // this thread's dim
   const int ctx = context_lens[seq];
   const int P = ctx > 0 ? (ctx + partition_size - 1) / partition_size : 0;
   const size_t base = ((size_t)seq * num_q_heads + h) * max_num_partitions;
@@ -455,13 +471,14 @@ splitk_reduce_kernel(const float* __restrict__ tmp_out, const float* __restrict_
     acc += (a0 + a1) + (a2 + a3);
     __syncthreads();  // s_w is rewritten by the next pass
   }
-  s_acc[grp][d] = acc;
+  s_acc[grp][dl] = acc;
   __syncthreads();
-  if (t < D) {
+  if (t < DC) {
     float o = 0.f;
 #pragma unroll
     for (int g = 0; g < GROUPS; ++g) o += s_acc[g][t];
-    out[((size_t)seq * num_q_heads + h) * D + t] = Elem<T>::from_float(l_run > 0.f ? o / l_run : 0.f);
+    out[((size_t)seq * num_q_heads + h) * D + blockIdx.z * DC + t] =
+        Elem<T>::from_float(l_run > 0.f ? o / l_run : 0.f);
   }
 }
 
@@ -546,9 +563,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream) {
 }
 
 hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_q_heads, a.num_seqs);
 #define PKA_REDUCE(T, D)                                                                                   \
-  hipLaunchKernelGGL((splitk_reduce_kernel<T, D>), grid, dim3(kReduceThreads), 0, stream, a.tmp_out,          \
+  hipLaunchKernelGGL((splitk_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs, ReduceGeom<D>::CHUNKS),    \
+                     dim3(kReduceThreads), 0, stream, a.tmp_out,                                              \
                      a.max_logits, a.exp_sums, a.context_lens, a.num_q_heads, a.partition_size,             \
                      a.max_num_partitions, a.out)
   if (a.bf16) {
