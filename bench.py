@@ -51,8 +51,8 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # (profiles/traffic_fetch_write.md), valid only for the kernel source they were
 # taken on: (source file, sha256 prefix, bytes).
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode.hip", "c629906f18649f21", 1191575008),
-    "splitk": ("decode.hip", "c629906f18649f21", 271019816),
+    "decode_step": ("decode.hip", "de774b36d6497090", 1191574048),
+    "splitk": ("decode.hip", "de774b36d6497090", 271015168),
     "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908832),
     "mixed": ("prefill.hip", "26823a696a320f6b", 50132520),
     "prefill_long": ("prefill.hip", "26823a696a320f6b", 201633088),
