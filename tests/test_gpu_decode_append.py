@@ -120,3 +120,16 @@ def test_append_rejects_bad_rows(pka):
     with pytest.raises(ValueError):
         pka.paged_attn_decode_append(ds.decode_q, ds.new_k.half(), ds.new_v, ds.k_cache, ds.v_cache,
                                      ds.decode_block_tables, ds.decode_context_lens, step.scale, max_context_len=9)
+
+
+def test_append_empty_batch_is_noop(pka):
+    step = W.make_decode_step(context_lens=[16], dtype=torch.bfloat16, seed=11, write_new=True)
+    ds = DevStep(step)
+    k0 = ds.k_cache.clone()
+    say("decode_append with zero sequences")
+    out = pka.paged_attn_decode_append(ds.decode_q[:0], ds.new_k[:0], ds.new_v[:0], ds.k_cache, ds.v_cache,
+                                       ds.decode_block_tables[:0], ds.decode_context_lens[:0], step.scale,
+                                       max_context_len=16)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert torch.equal(ds.k_cache.view(torch.int16), k0.view(torch.int16)), "an empty batch wrote to the pool"
