@@ -266,7 +266,7 @@ def bench_decode_step(args, pka):
     S, Hq, D = step.decode_q.shape
     max_ctx = step.max_context_len
     variant = pka.decode_choose_variant(S, step.num_kv_heads, max_ctx)
-    ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, max_ctx)), dtype=torch.uint8, device="cuda:0")
+    ws = pka.splitk_workspace(S, Hq, D, max_ctx, "cuda:0")
 
     # Comparison arm, timed first: the same step as two launches, the KV
     # write and then the dispatched decode reading the rows just written.
@@ -364,45 +364,83 @@ def bench_splitk(args, pka):
     P = Pools(step, args.rotate)
     S, Hq, D = step.decode_q.shape
     max_ctx = step.max_context_len
-    bufs = pka.splitk_buffers(S, Hq, D, max_ctx, "cuda:0")
+    assert pka.decode_choose_variant(S, step.num_kv_heads, max_ctx) == 2
+    dbytes = W.decode_bytes(step)
 
-    parts = [pka.paged_attn_decode_splitk(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, *bufs, prepare=True)
-             for r in range(P.R)]
-    reduce = pka.paged_attn_splitk_reduce(*bufs, P.cl, P.out, prepare=True)
+    # Comparison arm, timed first: the same decode as two launches (the
+    # partition pass, then the separate reduce kernel).
+    two_launch = None
+    if not args.no_arms:
+        bufs = pka.splitk_buffers(S, Hq, D, max_ctx, "cuda:0")
+        parts = [pka.paged_attn_decode_splitk(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, *bufs, prepare=True)
+                 for r in range(P.R)]
+        reduce = pka.paged_attn_splitk_reduce(*bufs, P.cl, P.out, prepare=True)
+
+        def launch2(i, ev):
+            r = i % P.R
+            if ev:
+                ev[0].record()
+            parts[r]()
+            if ev:
+                ev[1].record()
+            reduce()
+            if ev:
+                ev[2].record()
+
+        wall2, (part_ms, red_ms) = timed_loop(launch2, 2, args.steps, args.warmup)
+        two_launch = {"partition_us_per_call": round(part_ms * 1e3, 2), "reduce_us_per_call": round(red_ms * 1e3, 2),
+                      "eager_ms_per_step": round(wall2, 4),
+                      "partition_pass_gbs": round(dbytes / (part_ms * 1e-3) / 1e9, 1)}
+
+    # The step: the dispatched decode - one launch whose last partition of
+    # each (sequence, KV head) merges the partitions into the output.
+    ws = pka.splitk_workspace(S, Hq, D, max_ctx, "cuda:0")
+    decs = [pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out, workspace=ws,
+                                  prepare=True) for r in range(P.R)]
 
     def launch(i, ev):
         r = i % P.R
         if ev:
             ev[0].record()
-        parts[r]()
+        decs[r]()
         if ev:
             ev[1].record()
-        reduce()
-        if ev:
-            ev[2].record()
 
-    wall_ms, (part_ms, red_ms) = timed_loop(launch, 2, args.steps, args.warmup)
-    dbytes = W.decode_bytes(step)
+    st = {}
+    wall_ms, (dec_ms,) = timed_loop(launch, 1, args.steps, args.warmup, stats=st)
+    eager_ms = wall_ms
+    graph_ms = None
+    if not args.no_graph:
+        def step_fn(r):
+            return lambda: pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out,
+                                                 workspace=ws)
+        graph_ms = graph_step_ms([step_fn(r) for r in range(P.R)], args.steps, args.warmup)
+        wall_ms = graph_ms
     value = dbytes / (wall_ms * 1e-3) / 1e9
-    achieved = dbytes / (part_ms * 1e-3) / 1e9
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
     res = {
         "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
         "value": round(value, 2),
         "unit": "GB/s",
         "ms_per_step": round(wall_ms, 4),
-        "splitk_partition_us": round(part_ms * 1e3, 2),
-        "splitk_reduce_us": round(red_ms * 1e3, 2),
+        "step_launch": "hip-graph replay" if graph_ms is not None else "eager",
+        "eager_ms_per_step": round(eager_ms, 4),
+        "decode_us_per_call": round(dec_ms * 1e3, 2),
+        "decode_us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][0]],
+        "two_launch_partition_then_reduce": two_launch,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "dtype": "bf16",
         "config": {
             "workload": "split-K paged decode, bf16, 4 seqs x 16384 ctx, 16q/8kv, head_dim 128, 256-token partitions",
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": step.num_kv_heads, "head_dim": D,
             "context_tokens": int(step.context_lens.sum()), "pool_copies_rotated": P.R, "seed": args.seed,
+            "decode_variant": "split-K, one launch (last partition merges)",
             "algorithmic_bytes": {"decode": dbytes},
         },
         "roofline": {
-            "kernel": "paged_decode_kernel (split-K partition pass)", "bound": "hbm", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "paged_decode_kernel (split-K partitions + in-kernel merge, one launch)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
         },
     }
     return res, step, False
@@ -414,7 +452,7 @@ def bench_mixed(args, pka):
     nd = step.num_decode
     S, Hq, D = step.decode_q.shape
     max_dec = int(step.decode_context_lens.max())
-    ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, max_dec)), dtype=torch.uint8, device="cuda:0")
+    ws = pka.splitk_workspace(S, Hq, D, max_dec, "cuda:0")
     qd, qp = P.q[:nd], P.q[nd:]
     od, op = P.out[:nd], P.out[nd:]
     btd, btp = P.bt[:nd], P.bt[nd:]
@@ -672,7 +710,7 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
         step = W.config_1(seed=args.seed) if name == "single" else W.config_2(ctx, seed=args.seed)
         P = Pools(step, args.rotate or 2)
         S, Hq, D = step.decode_q.shape
-        ws = torch.empty(max(1, pka.splitk_workspace_bytes(S, Hq, D, ctx)), dtype=torch.uint8, device="cuda:0")
+        ws = pka.splitk_workspace(S, Hq, D, ctx, "cuda:0")
 
         decs = [pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, ctx, out=P.out, workspace=ws,
                                       prepare=True) for r in range(P.R)]

@@ -195,29 +195,43 @@ int32_t pka_paged_attn_splitk_reduce(const float* tmp_out, const float* max_logi
 
 /*
  * Bytes of workspace the dispatched decode needs when it takes the split-K
- * path: tmp_out, max_logits and exp_sums for
- * max_num_partitions = ceil(max_context_len / PKA_PARTITION_SIZE), each
- * region 256-byte aligned.  Pure host function.
+ * path: a 64 KiB header of arrival counters, then tmp_out, max_logits and
+ * exp_sums for max_num_partitions = ceil(max_context_len / PKA_PARTITION_SIZE),
+ * each region 256-byte aligned.  Pure host function.
  */
 size_t pka_splitk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len);
 
 /*
- * Decode dispatcher ([ME] "A dispatcher picks v2 when the batch is too small
- * to fill the GPU (few sequences or long contexts)").  Returns 1 (single
- * pass) or 2 (split-K) for num_seqs * num_kv_heads workgroups on num_cus
- * compute units with contexts up to max_context_len.  Pure host function.
+ * Decode dispatcher ([ME] "Custom CUDA kernels": v2 is chosen when the batch
+ * alone would leave the GPU idle, i.e. few sequences or long contexts).
+ * Returns 1 (single pass) or 2 (split-K) for num_seqs * num_kv_heads
+ * workgroups on num_cus compute units with contexts up to max_context_len.
+ * Pure host function.
  */
 int32_t pka_decode_choose_variant(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                   int32_t num_cus);
 
 /*
- * Paged decode with dispatch: runs v1, or split-K + reduce, as
- * pka_decode_choose_variant picks for this device.  max_context_len is a host
- * upper bound on context_lens.  The split-K path carves its buffers from
+ * Paged decode with dispatch: runs v1, or split-K with its partition merge,
+ * as pka_decode_choose_variant picks for this device.  max_context_len is a
+ * host upper bound on context_lens.  The split-K path carves its buffers from
  * `workspace` (device memory, at least pka_splitk_workspace_bytes bytes,
  * 256-byte aligned); the v1 path ignores it.  PKA_ERR_WORKSPACE if split-K is
  * chosen and the workspace is missing or too small.
+ *
+ * Split-K runs as ONE launch when num_seqs * num_kv_heads <= 16384: each
+ * (sequence, KV head) has an arrival counter in the workspace's first 64 KiB;
+ * a partition workgroup stores its state (same format as
+ * pka_paged_attn_decode_splitk), counts itself, and the one that arrives last
+ * merges the sequence's partitions into `out` (the rule of
+ * pka_paged_attn_splitk_reduce).  Larger batches run the partition pass and
+ * the reduce as two launches.
+ * Workspace contract: the first 64 KiB must be zero before the first call
+ * that uses the workspace (e.g. hipMemset once after allocating it); every
+ * call leaves them zero again, also under HIP-graph replay, so a workspace is
+ * reused without clearing.  The rest is scratch.  Calls that share a
+ * workspace must not run concurrently.
  */
 int32_t pka_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,
@@ -304,8 +318,8 @@ int32_t pka_device_cu_count(void);
 /*
  * Host-side paged block manager (MiniLLM Runtime: "Features" - block
  * allocation, release, reuse, reference counting, prefix-cache lookup with
- * shared ownership; mini_engine "Features": blocks hashed as soon as they
- * fill; miniserve "Architecture": KVCacheManager with chained hashes,
+ * shared ownership; mini_engine "Features": a block gets its hash the moment
+ * it is full; miniserve "Architecture": KVCacheManager with chained hashes,
  * refcounts and an LRU free list, and its request-state diagram).  Pure host
  * code, no GPU calls; one manager per KV pool, not thread-safe.
  *

@@ -9,9 +9,9 @@ What it models, and where the pages describe it:
 * MiniLLM Runtime ("Features" list; "Component graph"): KV block allocation,
   release, reuse and reference counting; per-request block tables; prefix
   cache lookup with shared block ownership.
-* mini_engine ("Features", Serving): hash-based prefix caching where blocks
-  are hashed as soon as they fill, so prefixes are shared even between
-  partially prefilled requests.
+* mini_engine ("Features", Serving): hash-based prefix caching in which a
+  block gets its hash the moment it is full, which lets requests that are
+  still part-way through their prefill share prefixes.
 * miniserve ("Architecture": KVCacheManager with paged blocks, chained
   hashes, refcounts and an LRU free list; the request state diagram and the
   "Engine" flowchart): find_cached_prefix() matches whole blocks through

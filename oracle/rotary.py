@@ -10,7 +10,8 @@ What it computes, and where the pages place it:
   "Where the remaining gap comes from" section lists RoPE among the separate
   eager kernels, and its "Roadmap" folds RoPE into the QKV split / KV-cache
   write.  miniserve's "Engine" flowchart orders the layer as fused qkv
-  projection, RoPE, then index_copy_ of the new K/V into the paged pool.
+  projection, RoPE, then an index_copy_ that puts each new token's K and V
+  rows into its pool slot.
 * So one step takes the fused projection output of T tokens, rows
   ``[q heads | k heads | v heads]``, rotates q and k by each token's position,
   returns the rotated q and scatters the rotated k and the unchanged v into

@@ -1,7 +1,8 @@
 """Paged KV attention for AMD Instinct MI355X (gfx950).
 
 A thin Python face over libpka.so (C ABI in include/pka.h): KV-cache write,
-paged decode (single pass, split-K + reduce, and the dispatcher over both) and
+paged decode (single pass, split-K with its partition reduce, and the
+dispatcher over both) and
 paged prefill over ragged, causally masked chunks.  Tensors are torch GPU
 tensors; the work runs in hand-written HIP kernels.  There is no CPU path:
 importing the package without the built library raises ImportError.
@@ -26,9 +27,11 @@ from ._lib import (  # noqa: F401
     paged_attn_prefill,
     paged_attn_splitk_reduce,
     prefill_split_keys,
+    prefill_workspace,
     prefill_workspace_bytes,
     rope_table,
     splitk_buffers,
+    splitk_workspace,
     splitk_workspace_bytes,
     version,
 )

@@ -452,6 +452,15 @@ def splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len) -> 
     return int(lib.pka_splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
 
 
+def splitk_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device) -> torch.Tensor:
+    """A workspace for the dispatched decode: uint8 device buffer of
+    splitk_workspace_bytes(...) bytes, zero-filled once here (the split-K
+    arrival counters at its start must be zero before the first call; every
+    call leaves them zero, so the buffer is reused as is)."""
+    n = max(1, splitk_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
 def decode_choose_variant(num_seqs, num_kv_heads, max_context_len, num_cus=None) -> int:
     if num_cus is None:
         num_cus = device_cu_count()
@@ -460,16 +469,18 @@ def decode_choose_variant(num_seqs, num_kv_heads, max_context_len, num_cus=None)
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
                       workspace=None, prepare=False):
-    """Paged decode with the library's dispatcher (single pass or split-K +
-    reduce).  max_context_len: host upper bound on context_lens.  workspace:
-    optional uint8 device buffer of splitk_workspace_bytes(...) bytes; one is
-    allocated when the split-K path needs it and none is given."""
+    """Paged decode with the library's dispatcher (single pass, or split-K
+    with its partition merge).  max_context_len: host upper bound on
+    context_lens.  workspace: optional uint8 device buffer of
+    splitk_workspace_bytes(...) bytes whose first 64 KiB are zero before its
+    first use (splitk_workspace() makes one); one is allocated when the split-K
+    path needs it and none is given."""
     _decode_common(q, k_cache, v_cache, block_tables, context_lens)
     out = _out_like(q, out)
     S, Hq, D = q.shape
     need = splitk_workspace_bytes(S, Hq, D, max_context_len)
     if workspace is None and decode_choose_variant(S, k_cache.shape[2], max_context_len) == 2:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
@@ -497,7 +508,7 @@ def paged_attn_decode_append(q, key, value, k_cache, v_cache, block_tables, cont
     out = _out_like(q, out)
     need = splitk_workspace_bytes(S, Hq, D, max_context_len)
     if workspace is None and decode_choose_variant(S, k_cache.shape[2], max_context_len) == 2:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0
     if workspace is not None:
         _require(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
@@ -512,6 +523,14 @@ def paged_attn_decode_append(q, key, value, k_cache, v_cache, block_tables, cont
 def prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
     return int(lib.pka_prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
                                                max_context_len))
+
+
+def prefill_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                      device) -> torch.Tensor:
+    """A workspace for paged_attn_prefill: uint8 device buffer of
+    prefill_workspace_bytes(...) bytes (at least 1)."""
+    n = max(1, prefill_workspace_bytes(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len))
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def prefill_split_keys(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, max_context_len) -> int:

@@ -5,8 +5,10 @@ into one shared library next to this file.  Packed-fp32 code generation is
 switched off (-packed-fp32-ops): the compiler would otherwise fuse pairs of
 fp32 operations into v_pk_* instructions.
 
-Usage: python paged_kv_attention_21_amd/build.py   (run by path, so the
-package - which loads the library - is not imported before it is rebuilt).
+Usage: python paged_kv_attention_21_amd/build.py [--changed] [-v]   (run by
+path, so the package - which loads the library - is not imported before it is
+rebuilt).  --changed recompiles only the objects older than their source or
+than any header under csrc/ or include/; the default recompiles everything.
 """
 
 from __future__ import annotations
@@ -25,7 +27,10 @@ BUILD_DIR = os.path.join(ROOT, "_build", "pka")
 LIB_NAME = "libpka.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "rope_kv.hip", "block_manager.cpp"]
+# The decode kernels are instantiated per (element type, head size) in their
+# own translation units so they compile in parallel.
+DECODE_UNITS = [f"decode_{t}_d{d}.hip" for t in ("f16", "bf16") for d in (64, 128, 256)]
+SOURCES = ["api.cpp", "kv_write.hip", "decode.hip", *DECODE_UNITS, "prefill.hip", "rope_kv.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -57,18 +62,32 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libpka.so; returns the library path."""
+def _newest_header() -> float:
+    newest = 0.0
+    for d in (CSRC, INCLUDE):
+        for f in os.listdir(d):
+            if f.endswith(".h"):
+                newest = max(newest, os.path.getmtime(os.path.join(d, f)))
+    return newest
+
+
+def build(verbose: bool = False, jobs: int | None = None, changed_only: bool = False) -> str:
+    """Compile every source (or, with changed_only, the stale ones) and link
+    libpka.so; returns the library path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
+    headers = _newest_header()
     objs = []
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         objs.append(obj)
+        path = os.path.join(CSRC, src)
+        if changed_only and os.path.exists(obj) and os.path.getmtime(obj) > max(os.path.getmtime(path), headers):
+            continue
         lang = ["-x", "hip"]
-        cmds.append([hipcc, *lang, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    jobs = jobs or min(len(cmds), os.cpu_count() or 4)
+        cmds.append([hipcc, *lang, *COMMON_FLAGS, "-c", path, "-o", obj])
+    jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 4))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -80,4 +99,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, changed_only="--changed" in sys.argv))

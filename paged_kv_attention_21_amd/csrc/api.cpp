@@ -84,6 +84,8 @@ int32_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, 
   return PKA_OK;
 }
 
+int32_t splitk_into(pka::DecodeArgs& a, int32_t P, char* workspace, hipStream_t s);
+
 // Dispatched decode (single pass, or split-K + reduce); new_k / new_v non-null
 // append one token per sequence (pka_paged_attn_decode_append).
 int32_t decode_dispatch(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -112,30 +114,39 @@ int32_t decode_dispatch(const void* q, const void* k_cache, const void* v_cache,
   const int32_t cus = pka_device_cu_count();
   const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len, cus);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (variant == 1) return hip_status(pka::launch_decode(a, false, s));
+  if (variant == 1) return hip_status(pka::launch_decode(a, pka::kLaunchSingle, s));
 
   const int32_t P = num_partitions(max_context_len);
   if (P > 65535) return PKA_ERR_UNSUPPORTED;
   const size_t need = pka_splitk_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len);
   if (!workspace || workspace_bytes < need) return PKA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PKA_ERR_ALIGN;
-  const size_t rows = (size_t)num_seqs * num_q_heads * P;
-  char* w = static_cast<char*>(workspace);
+  return splitk_into(a, P, static_cast<char*>(workspace), s);
+}
+
+int32_t splitk_into(pka::DecodeArgs& a, int32_t P, char* w, hipStream_t s) {
+  // Workspace: the counter header, then tmp_out, max_logits, exp_sums.
+  const size_t rows = (size_t)a.num_seqs * a.num_kv_heads * a.group * P;
   a.max_num_partitions = P;
+  a.counters = reinterpret_cast<uint32_t*>(w);
+  w += pka::kSplitCounterBytes;
   a.tmp_out = reinterpret_cast<float*>(w);
-  a.max_logits = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)));
-  a.exp_sums = reinterpret_cast<float*>(w + align256(rows * cache.head_dim * sizeof(float)) +
+  a.max_logits = reinterpret_cast<float*>(w + align256(rows * a.head_dim * sizeof(float)));
+  a.exp_sums = reinterpret_cast<float*>(w + align256(rows * a.head_dim * sizeof(float)) +
                                         align256(rows * sizeof(float)));
-  hipError_t e = pka::launch_decode(a, true, s);
+  // One launch when the counters fit the header; else partitions + reduce.
+  if ((int64_t)a.num_seqs * a.num_kv_heads <= pka::kSplitCounterSlots)
+    return hip_status(pka::launch_decode(a, pka::kLaunchSplitFused, s));
+  hipError_t e = pka::launch_decode(a, pka::kLaunchSplit, s);
   if (e != hipSuccess) return PKA_ERR_HIP;
   pka::ReduceArgs r{};
   r.tmp_out = a.tmp_out;
   r.max_logits = a.max_logits;
   r.exp_sums = a.exp_sums;
-  r.context_lens = context_lens;
-  r.num_seqs = num_seqs;
-  r.num_q_heads = num_q_heads;
-  r.head_dim = cache.head_dim;
+  r.context_lens = a.context_lens;
+  r.num_seqs = a.num_seqs;
+  r.num_q_heads = a.num_kv_heads * a.group;
+  r.head_dim = a.head_dim;
   r.partition_size = pka::kPartitionSize;
   r.max_num_partitions = P;
   r.bf16 = a.bf16;
@@ -189,6 +200,7 @@ int32_t pka_kv_cache_write(const void* key, const void* value, const int64_t* sl
   a.slot_mapping = slot_mapping;
   a.num_tokens = num_tokens;
   a.row_bytes = cache.num_kv_heads * cache.head_dim * elem_size(cache.dtype);
+  a.num_slots = (int64_t)cache.num_blocks * cache.block_size;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   return hip_status(pka::launch_kv_write(a, static_cast<hipStream_t>(stream)));
@@ -233,6 +245,8 @@ int32_t pka_fused_rope_kv_write(const void* qkv, int64_t qkv_row_stride, const i
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = cache.num_kv_heads;
   a.head_dim = cache.head_dim;
+  a.max_position = max_position;
+  a.num_slots = (int64_t)cache.num_blocks * cache.block_size;
   a.bf16 = cache.dtype == PKA_BF16;
   a.q_out = static_cast<uint16_t*>(q_out);
   a.k_cache = static_cast<uint16_t*>(k_cache);
@@ -254,7 +268,7 @@ int32_t pka_paged_attn_decode_v1(const void* q, const void* k_cache, const void*
   if (!aligned16(out)) return PKA_ERR_ALIGN;
   if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
   a.out = static_cast<uint16_t*>(out);
-  return hip_status(pka::launch_decode(a, false, static_cast<hipStream_t>(stream)));
+  return hip_status(pka::launch_decode(a, pka::kLaunchSingle, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pka_paged_attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
@@ -276,7 +290,7 @@ int32_t pka_paged_attn_decode_splitk(const void* q, const void* k_cache, const v
   a.tmp_out = tmp_out;
   a.max_logits = max_logits;
   a.exp_sums = exp_sums;
-  return hip_status(pka::launch_decode(a, true, static_cast<hipStream_t>(stream)));
+  return hip_status(pka::launch_decode(a, pka::kLaunchSplit, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pka_paged_attn_splitk_reduce(const float* tmp_out, const float* max_logits, const float* exp_sums,
@@ -309,7 +323,7 @@ size_t pka_splitk_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * num_partitions(max_context_len);
-  return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+  return pka::kSplitCounterBytes + align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
 }
 
 int32_t pka_decode_choose_variant(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

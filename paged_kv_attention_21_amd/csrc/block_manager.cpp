@@ -3,7 +3,7 @@
 //
 // What it does (MiniLLM Runtime: "Features" - block allocation, release,
 // reuse, reference counting, prefix-cache lookup with shared ownership;
-// mini_engine "Features": blocks are hashed as soon as they fill; miniserve
+// mini_engine "Features": a block gets its hash the moment it is full; miniserve
 // "Architecture" - KVCacheManager with chained hashes, refcounts and an LRU
 // free list - and its request-state diagram and "Engine" flowchart):
 //

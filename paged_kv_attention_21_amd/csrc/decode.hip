@@ -1,586 +1,37 @@
-// Paged decode attention for gfx950.
-//
-// What it computes (MiniLLM Runtime, "CUDA PagedAttention scope"; mini_engine,
-// "Custom CUDA kernels", paged decode v1 and v2): for one query row per
-// sequence, softmax(scale * q . k_t) over the sequence's context, then the
-// weighted sum of v_t, reading every K/V row in place through the block table
-// (MiniLLM Runtime, "Core class relationships").
-//
-// Work decomposition.  One workgroup per (KV head, sequence) - or per
-// (KV head, 256-token partition, sequence) for split-K.  The G query heads of
-// the GQA group ride along, so every K/V byte is loaded once and used G times.
-// The workgroup's W wavefronts take the range's KV blocks round-robin.  The
-// single pass runs the sequences longest first (see heavy_first_seq).
-//
-// Lane layout inside a wavefront.  One 16-byte load per lane (8 elements)
-// makes a token row of D elements span LPT = D / 8 lanes, so one wave load
-// covers TPL = 64 / LPT tokens and a 16-token block of one head takes
-// LPB = 16 / TPL loads per tensor (D = 128: 16 lanes, 4 tokens, 4 loads);
-// 8- and 32-token blocks take half and twice as many.
-// Each group of LPT lanes ("row") sums its dot-product pieces with DPP and
-// keeps its own online-softmax state (max, exp-sum, 8 accumulator dims per
-// head) over the tokens it sees; rows, then wavefronts, are merged once at the
-// end with the same max/exp-sum rule the split-K reduce uses.
-//
-// Memory: the caches are token-major ([block][slot][kv head][dim]), so a
-// (block, head) is 16 rows of D*2 bytes at a stride of num_kv_heads*D*2 bytes;
-// each row is fetched as whole 16-byte pieces by consecutive lanes.  Each
-// wavefront keeps the next block's K and V loads in flight while it computes
-// on the current one.  K/V are read exactly once, so the loads are marked
-// non-temporal (measured on MI355X: the paged read pattern streams at ~5.9 TB/s
-// with them and ~5.2 TB/s without).  Block-table entries are fetched 64 at a time with one
-// vector load per wavefront and broadcast with readlane.
-//
-// Numerics: q.k in fp32 with v_dot2 on the raw fp16/bf16 pairs; softmax in the
-// base-2 domain (scale * log2 e folded into the logit); fp32 accumulation;
-// tokens past the context are selected out (never multiplied by a zero
-// weight), so NaN garbage in unowned slots cannot leak in.
+// Decode dispatch: picks the (element type, head size) instance of the decode
+// kernels (compiled separately in decode_<type>_d<size>.hip, whose kernels are
+// defined in decode_impl.h).
 
-#include "device_common.h"
-#include "launch.h"
-
-#include <type_traits>
+#include "decode_impl.h"
 
 namespace pka {
 
-template <int D, int BS>
-struct DecodeLayout {
-  static constexpr int LPT = D / 8;       // lanes per token row
-  static constexpr int TPL = kWave / LPT;  // token rows per wave load
-  static constexpr int LPB = BS / TPL;     // wave loads per block per tensor
-  static_assert(kWave % LPT == 0 && BS % TPL == 0 && kPartitionSize % BS == 0, "unsupported head_dim / block");
-};
+PKA_DECODE_FOR_ALL(PKA_DECODE_EXTERN)
 
-// Heavy-first order of the single-pass grid.  Workgroups start in grid order
-// as earlier ones finish, and a long sequence that starts last sets the
-// kernel's tail, so grid row r is given the r-th sequence in decreasing
-// order of context length - approximated by kOrderBuckets equal buckets of
-// [0, max_ctx], equal buckets in index order (longest-processing-time-first
-// list scheduling).  Every workgroup derives the same order from
-// context_lens: one load per sequence and thread group, a histogram in LDS
-// and one scan by the first wavefront.  Returns a wavefront-uniform index.
-constexpr int kOrderBuckets = kWave;  // one bucket per lane of the scan
-template <int NT>
-__device__ __forceinline__ int heavy_first_seq(const int32_t* __restrict__ context_lens, int num_seqs, int max_ctx,
-                                               int rank, int* lds /* kOrderBuckets + 1 ints */) {
-  const int tid = threadIdx.x;
-  auto bucket = [&](int i) {  // 0 holds the longest contexts
-    const long long c = max(context_lens[i], 0);
-    const int b = (int)(c * kOrderBuckets / ((long long)max_ctx + 1));
-    return kOrderBuckets - 1 - min(b, kOrderBuckets - 1);
-  };
-  if (tid < kOrderBuckets) lds[tid] = 0;
-  __syncthreads();
-  for (int i = tid; i < num_seqs; i += NT) atomicAdd(&lds[bucket(i)], 1);
-  __syncthreads();
-  if (tid < kWave) {
-    const int lane = tid;
-    const int cnt = lds[lane];
-    int incl = cnt;  // inclusive prefix sum over the buckets
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    const int excl = incl - cnt;
-    const unsigned long long hit = __ballot(cnt > 0 && excl <= rank && rank < incl);
-    int found = rank;  // unreachable fallback: the given order
-    if (hit) {
-      const int k = __ffsll((long long)hit) - 1;  // the bucket holding position `rank`
-      int target = rank - __shfl(excl, k);
-      for (int base = 0; base < num_seqs; base += kWave) {
-        const int i = base + lane;
-        const bool match = i < num_seqs && bucket(i) == k;
-        const unsigned long long mask = __ballot(match);
-        const int n = __popcll(mask);
-        if (target < n) {
-          const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-          found = base + __ffsll((long long)__ballot(match && pos == target)) - 1;
-          break;
-        }
-        target -= n;
-      }
-    }
-    if (lane == 0) lds[kOrderBuckets] = found;
-  }
-  __syncthreads();
-  return __builtin_amdgcn_readfirstlane(lds[kOrderBuckets]);
-}
-
-// BS = tokens per KV block (8, 16 or 32).
-template <typename T, int D, int G, int W, bool SPLIT, int BS>
-__global__ void __launch_bounds__(W * kWave)
-paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-                    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-                    const int32_t* __restrict__ context_lens, int32_t max_blocks_per_seq,
-                    int32_t num_kv_heads, float scale_log2, uint16_t* __restrict__ out,
-                    float* __restrict__ tmp_out, float* __restrict__ max_logits,
-                    float* __restrict__ exp_sums, int32_t max_num_partitions, int32_t order_max_ctx,
-                    const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v,
-                    uint16_t* __restrict__ k_store, uint16_t* __restrict__ v_store, int32_t pair_from) {
-  using L = DecodeLayout<D, BS>;
-  constexpr int kBlockSize = BS;
-  using E = Elem<T>;
-  constexpr int LPT = L::LPT, TPL = L::TPL, LPB = L::LPB;
-
-  const int kvh = blockIdx.x;
-  const int part = SPLIT ? (int)blockIdx.y : 0;
-  int seq = SPLIT ? (int)blockIdx.z : (int)blockIdx.y;
-  if constexpr (!SPLIT) {
-    __shared__ int order_lds[kOrderBuckets + 1];
-    // When the whole grid is resident at once and some compute units hold two
-    // workgroups (see launch_decode_t), the rows that take a unit's second
-    // slot run in reverse rank order, so a unit pairs a long sequence with a
-    // short one instead of two long ones.
-    if (pair_from > 0 && seq >= pair_from) seq = (int)gridDim.y + pair_from - 1 - seq;
-    if (order_max_ctx > 0) seq = heavy_first_seq<W * kWave>(context_lens, gridDim.y, order_max_ctx, seq, order_lds);
-  }
-  const int num_q_heads = num_kv_heads * G;
-
-  const int ctx = context_lens[seq];
-  int tok_begin = 0, tok_end = ctx;
-  if constexpr (SPLIT) {
-    tok_begin = part * kPartitionSize;
-    if (tok_begin >= ctx) return;  // past this sequence's end: nothing to write
-    tok_end = min(ctx, tok_begin + kPartitionSize);
-  }
-  const int lb_begin = tok_begin / kBlockSize;
-  const int nblk = tok_end > tok_begin ? (tok_end - tok_begin + kBlockSize - 1) / kBlockSize : 0;
-  const int last_valid = tok_end - (lb_begin + nblk - 1) * kBlockSize;  // tokens in the range's last block
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = wave_id();
-  const int row = lane / LPT;
-  const int col = lane % LPT;  // this lane's 8 dims: col*8 .. col*8+7
-
-  // Appended token (when new_k is given): position ctx - 1 of every sequence
-  // is the row new_k / new_v [seq][kvh] - the decode step's KV-cache write
-  // folded into the attention that reads it.  The wavefront that consumes
-  // the range's last block takes that position's K/V from registers (the
-  // cached copy may be stale or NaN until then: it is loaded and selected
-  // out, never read back) and stores the row to its slot, whose block it
-  // already holds, so no extra table lookup delays the start of the loop.
-  const bool append = new_k != nullptr && ctx > 0 && tok_end == ctx;
-  uint4 app_k = make_uint4(0, 0, 0, 0), app_v = app_k;
-  if (append) {
-    const size_t src = ((size_t)seq * num_kv_heads + kvh) * D + col * 8;
-    app_k = *reinterpret_cast<const uint4*>(new_k + src);
-    app_v = *reinterpret_cast<const uint4*>(new_v + src);
-  }
-
-  // q pieces of the G heads of this group.
-  uint32_t qv[G][4];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 t = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + kvh * G + g) * D + col * 8);
-    qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
-  }
-
-  float m[G], lsum[G], acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegBig;
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[g][d] = 0.f;
-  }
-
-  const size_t row_elems = (size_t)num_kv_heads * D;        // elements between consecutive slots
-  const size_t block_bytes = row_elems * kBlockSize * 2;    // bytes per physical block
-  // Per-lane byte offset of load i inside a (block, head): row (i*TPL + row), dims col*8.
-  uint32_t lane_off[LPB];
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
-  const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
-  const int32_t* tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
-
-  // This wavefront's blocks are wave, wave + W, wave + 2W, ... (< nblk).
-  const int nb_wave = wave < nblk ? (nblk - wave + W - 1) / W : 0;
-
-  auto issue = [&](int pb, uint4 (&kk)[LPB], uint4 (&vv)[LPB]) {
-    const char* kb = kbase + (size_t)pb * block_bytes;
-    const char* vb = vbase + (size_t)pb * block_bytes;
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) kk[i] = load_nt16(kb + lane_off[i]);
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) vv[i] = load_nt16(vb + lane_off[i]);
-  };
-
-  // MASKED is only taken for the range's last block when it is partial.
-  auto consume_t = [&](auto masked, const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int nvalid) {
-    constexpr bool MASKED = decltype(masked)::value;
-    float s[G][LPB];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      const bool valid = !MASKED || (i * TPL + row) < nvalid;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = E::dot2(qv[g][0], kk[i].x, 0.f);
-        d = E::dot2(qv[g][1], kk[i].y, d);
-        d = E::dot2(qv[g][2], kk[i].z, d);
-        d = E::dot2(qv[g][3], kk[i].w, d);
-        d = group_sum<LPT>(d) * scale_log2;
-        s[g][i] = valid ? d : -INFINITY;
-      }
-    }
-    float p[G][LPB];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, s[g][i]);
-      const float alpha = fast_exp2(m[g] - mx);
-      m[g] = mx;
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        p[g][i] = fast_exp2(s[g][i] - mx);
-        ps += p[g][i];
-      }
-      lsum[g] = lsum[g] * alpha + ps;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      const bool valid = !MASKED || (i * TPL + row) < nvalid;
-      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-      float vf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = E::lo(w4[e]);
-        vf[2 * e + 1] = E::hi(w4[e]);
-      }
-      if (MASKED && !valid) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) vf[d] = 0.f;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[g][d] = fmaf(p[g][i], vf[d], acc[g][d]);
-    }
-  };
-
-  // pb: the block's physical id (used only for the appended token's store).
-  auto consume = [&](const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int blk, int pb) {
-    if (blk == nblk - 1 && append) {
-      // The range's last block holds the appended token at row last_valid - 1:
-      // load i = (last_valid - 1) / TPL, lane row (last_valid - 1) % TPL.
-      uint4 ka2[LPB], va2[LPB];
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        const bool mine = i * TPL + row == last_valid - 1;
-        ka2[i] = mine ? app_k : kk[i];
-        va2[i] = mine ? app_v : vv[i];
-      }
-      if (row == (last_valid - 1) % TPL) {
-        const uint32_t off = lane_off[0] + (uint32_t)(((last_valid - 1) / TPL) * TPL * row_elems * 2);
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
-                                  off) = app_k;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
-                                  off) = app_v;
-      }
-      if (last_valid < kBlockSize)
-        consume_t(std::true_type{}, ka2, va2, last_valid);
-      else
-        consume_t(std::false_type{}, ka2, va2, kBlockSize);
-    } else if (blk == nblk - 1 && last_valid < kBlockSize) {
-      consume_t(std::true_type{}, kk, vv, last_valid);
-    } else {
-      consume_t(std::false_type{}, kk, vv, kBlockSize);
-    }
-  };
-
-  // Main loop, double-buffered over this wavefront's blocks: while a block is
-  // consumed the next one's 2*LPB loads are in flight.  The steady-state body
-  // issues unconditionally, so every consume in it waits for its own loads
-  // only; the 1-3 blocks left at the end of a window are peeled (their waits
-  // may be conservative, and no block is fetched twice).  Table entries come
-  // 64 at a time (lane k holds the entry of the wave's block j0 + k).
-  uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
-  for (int j0 = 0; j0 < nb_wave; j0 += kWave) {
-    const int jn = min(kWave, nb_wave - j0);
-    const int tbl_win = lane < jn ? tbl[wave + (j0 + lane) * W] : 0;
-    const int blk_base = wave + j0 * W;  // range-relative index of the window's block 0
-    issue(uniform_lane(tbl_win, 0), ka, va);
-    if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
-    int j = 0;
-    for (; j + 3 < jn; j += 2) {
-      consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
-      issue(uniform_lane(tbl_win, j + 2), ka, va);
-      consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
-      issue(uniform_lane(tbl_win, j + 3), kb2, vb2);
-    }
-    const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
-    consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
-    if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
-    if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
-    if (rem == 3) consume(ka, va, blk_base + (j + 2) * W, uniform_lane(tbl_win, j + 2));
-  }
-
-  // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(lsum[g], off);
-      const float mm = fmaxf(m[g], mo);
-      const float fa = fast_exp2(m[g] - mm);
-      const float fb = fast_exp2(mo - mm);
-      lsum[g] = lsum[g] * fa + lo * fb;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[g][d] = acc[g][d] * fa + __shfl_xor(acc[g][d], off) * fb;
-      m[g] = mm;
-    }
-  }
-
-  // Merge the wavefronts through LDS, normalise and store.
-  __shared__ float s_m[W][G], s_l[W][G];
-  __shared__ float s_acc[W][G][D];
-  if (row == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) s_acc[wave][g][col * 8 + d] = acc[g][d];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = m[g];
-      s_l[wave][g] = lsum[g];
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += W * kWave) {
-    const int g = t / D, d = t % D;
-    float mm = kNegBig;
-#pragma unroll
-    for (int w = 0; w < W; ++w) mm = fmaxf(mm, s_m[w][g]);
-    float lt = 0.f, at = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float f = fast_exp2(s_m[w][g] - mm);
-      lt += s_l[w][g] * f;
-      at += s_acc[w][g][d] * f;
-    }
-    const int h = kvh * G + g;
-    const float o = lt > 0.f ? at / lt : 0.f;
-    if constexpr (SPLIT) {
-      const size_t idx = ((size_t)seq * num_q_heads + h) * max_num_partitions + part;
-      tmp_out[idx * D + d] = o;
-      if (d == 0) {
-        max_logits[idx] = mm * kLn2;  // back to natural-log units
-        exp_sums[idx] = lt;
-      }
-    } else {
-      out[((size_t)seq * num_q_heads + h) * D + d] = E::from_float(o);
-    }
-  }
-}
-
-// Split-K reduce: one workgroup per (query head, sequence, chunk of
-// ReduceGeom::DC dims).  Partitions are taken in passes of up to kReduceChunk:
-// the threads find the pass's max logit and weights w_p = l_p exp(m_p - M) in
-// parallel (weights kept in LDS; every dim chunk recomputes them, a few loads
-// per partition), then thread t accumulates dim t % DC of the chunk over
-// partitions t / DC, t / DC + GROUPS, ... with independent loads in flight; a
-// running max rescales earlier passes.
-constexpr int kReduceThreads = 256;
-constexpr int kReduceChunk = 1024;
-
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  __syncthreads();  // scratch may still be read by a previous reduction
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  v = scratch[0];
-#pragma unroll
-  for (int w = 1; w < kReduceThreads / kWave; ++w) v = is_max ? fmaxf(v, scratch[w]) : v + scratch[w];
-  return v;
-}
-
-// Dims per reduce workgroup: the head's dims are spread over D / kReduceDims
-// workgroups, so a few (sequence, head) pairs still fill the GPU and each
-// thread walks a quarter of the partitions it would otherwise.
-#ifndef PKA_REDUCE_DIMS
-#define PKA_REDUCE_DIMS 32
-#endif
-template <int D>
-struct ReduceGeom {
-  static constexpr int DC = D < PKA_REDUCE_DIMS ? D : PKA_REDUCE_DIMS;  // dims per workgroup
-  static constexpr int CHUNKS = D / DC;
-};
-
-template <typename T, int D>
-__global__ void __launch_bounds__(kReduceThreads)
-splitk_reduce_kernel(const float* __restrict__ tmp_out, const float* __restrict__ max_logits,
-                     const float* __restrict__ exp_sums, const int32_t* __restrict__ context_lens,
-                     int32_t num_q_heads, int32_t partition_size, int32_t max_num_partitions,
-                     uint16_t* __restrict__ out) {
-  constexpr int DC = ReduceGeom<D>::DC;
-  constexpr int GROUPS = kReduceThreads / DC;
-  __shared__ float s_w[kReduceChunk];
-  __shared__ float s_red[kReduceThreads / kWave];
-  __shared__ float s_acc[GROUPS][DC];
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int t = threadIdx.x;
-  const int dl = t % DC, grp = t / DC;
-  const int d = blockIdx.z * DC + dl;  // this thread's dim
-  const int ctx = context_lens[seq];
-  const int P = ctx > 0 ? (ctx + partition_size - 1) / partition_size : 0;
-  const size_t base = ((size_t)seq * num_q_heads + h) * max_num_partitions;
-
-  float m_run = -INFINITY, l_run = 0.f, acc = 0.f;
-  for (int p0 = 0; p0 < P; p0 += kReduceChunk) {
-    const int n = min(kReduceChunk, P - p0);
-    float mx = -INFINITY;
-    for (int p = t; p < n; p += kReduceThreads) mx = fmaxf(mx, max_logits[base + p0 + p]);
-    mx = block_reduce(mx, true, s_red);
-    const float m_new = fmaxf(m_run, mx);
-    const float rescale = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * kLog2e);
-    float ls = 0.f;
-    for (int p = t; p < n; p += kReduceThreads) {
-      const float w = exp_sums[base + p0 + p] * fast_exp2((max_logits[base + p0 + p] - m_new) * kLog2e);
-      s_w[p] = w;
-      ls += w;
-    }
-    ls = block_reduce(ls, false, s_red);  // its barriers also publish s_w
-    l_run = l_run * rescale + ls;
-    acc *= rescale;
-    m_run = m_new;
-    const float* po = tmp_out + (base + p0) * D + d;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int p = grp;
-    for (; p + 3 * GROUPS < n; p += 4 * GROUPS) {
-      a0 += s_w[p] * po[(size_t)p * D];
-      a1 += s_w[p + GROUPS] * po[(size_t)(p + GROUPS) * D];
-      a2 += s_w[p + 2 * GROUPS] * po[(size_t)(p + 2 * GROUPS) * D];
-      a3 += s_w[p + 3 * GROUPS] * po[(size_t)(p + 3 * GROUPS) * D];
-    }
-    for (; p < n; p += GROUPS) a0 += s_w[p] * po[(size_t)p * D];
-    acc += (a0 + a1) + (a2 + a3);
-    __syncthreads();  // s_w is rewritten by the next pass
-  }
-  s_acc[grp][dl] = acc;
-  __syncthreads();
-  if (t < DC) {
-    float o = 0.f;
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) o += s_acc[g][t];
-    out[((size_t)seq * num_q_heads + h) * D + blockIdx.z * DC + t] =
-        Elem<T>::from_float(l_run > 0.f ? o / l_run : 0.f);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// launchers
-// ---------------------------------------------------------------------------
-
-#ifndef PKA_DECODE_WAVES
-#define PKA_DECODE_WAVES 4
-#endif
-constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per single-pass decode workgroup
-#ifndef PKA_SPLIT_WAVES
-#define PKA_SPLIT_WAVES 4
-#endif
-constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partition workgroup
-// Heavy-first ordering scans all context lengths in every workgroup; above
-// this many sequences the grid order is kept.
-constexpr int kOrderMaxSeqs = 1024;
-
-template <typename T, int D, int G, int BS>
-static hipError_t launch_decode_t(const DecodeArgs& a, bool split, hipStream_t stream) {
-  const float scale_log2 = a.scale * kLog2e;
-  if (!split) {
-    dim3 grid(a.num_kv_heads, a.num_seqs);
-    // Longest-first pairing: a grid of more workgroups than compute units but
-    // no more than two per unit starts all at once, the first CUs / H rows
-    // taking one slot on every unit and the rest a second slot; those rows
-    // are reversed (measured on the 64-sequence decode of the mixed step:
-    // 7-11 % faster; grids of several rounds keep plain longest-first order).
-    const int64_t wgs = (int64_t)a.num_seqs * a.num_kv_heads;
-    int32_t pair_from = 0;
-    if (a.num_cus > 0 && wgs > a.num_cus && wgs <= 2 * (int64_t)a.num_cus) pair_from = a.num_cus / a.num_kv_heads;
-    if (pair_from >= a.num_seqs) pair_from = 0;
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, false, BS>), grid, dim3(kDecodeWaves * kWave), 0,
-                       stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
-                       a.num_kv_heads, scale_log2, a.out, nullptr, nullptr, nullptr, 0,
-                       a.num_seqs <= kOrderMaxSeqs ? a.order_max_ctx : 0, a.new_k, a.new_v, a.k_store, a.v_store,
-                       a.num_seqs <= kOrderMaxSeqs && a.order_max_ctx > 0 ? pair_from : 0);
+hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t stream) {
+  if (a.bf16) {
+    if (a.head_dim == 64) return launch_decode_td<BF16, 64>(a, mode, stream);
+    if (a.head_dim == 128) return launch_decode_td<BF16, 128>(a, mode, stream);
+    if (a.head_dim == 256) return launch_decode_td<BF16, 256>(a, mode, stream);
   } else {
-    dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, true, BS>), grid, dim3(kSplitWaves * kWave), 0,
-                       stream, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.max_blocks_per_seq,
-                       a.num_kv_heads, scale_log2, nullptr, a.tmp_out, a.max_logits, a.exp_sums,
-                       a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store, 0);
-  }
-  return hipGetLastError();
-}
-
-template <typename T, int D, int G>
-static hipError_t launch_decode_b(const DecodeArgs& a, bool split, hipStream_t stream) {
-  switch (a.block_size) {
-    case 8: return launch_decode_t<T, D, G, 8>(a, split, stream);
-    case 16: return launch_decode_t<T, D, G, 16>(a, split, stream);
-    case 32: return launch_decode_t<T, D, G, 32>(a, split, stream);
+    if (a.head_dim == 64) return launch_decode_td<F16, 64>(a, mode, stream);
+    if (a.head_dim == 128) return launch_decode_td<F16, 128>(a, mode, stream);
+    if (a.head_dim == 256) return launch_decode_td<F16, 256>(a, mode, stream);
   }
   return hipErrorInvalidValue;
-}
-
-template <typename T, int D>
-static hipError_t launch_decode_g(const DecodeArgs& a, bool split, hipStream_t stream) {
-  switch (a.group) {
-    case 1: return launch_decode_b<T, D, 1>(a, split, stream);
-    case 2: return launch_decode_b<T, D, 2>(a, split, stream);
-    case 4: return launch_decode_b<T, D, 4>(a, split, stream);
-    case 8: return launch_decode_b<T, D, 8>(a, split, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename T>
-static hipError_t launch_decode_d(const DecodeArgs& a, bool split, hipStream_t stream) {
-  switch (a.head_dim) {
-    case 64: return launch_decode_g<T, 64>(a, split, stream);
-    case 128: return launch_decode_g<T, 128>(a, split, stream);
-    case 256: return launch_decode_g<T, 256>(a, split, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream) {
-  return a.bf16 ? launch_decode_d<BF16>(a, split, stream) : launch_decode_d<F16>(a, split, stream);
 }
 
 hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream) {
-#define PKA_REDUCE(T, D)                                                                                   \
-  hipLaunchKernelGGL((splitk_reduce_kernel<T, D>), dim3(a.num_q_heads, a.num_seqs, ReduceGeom<D>::CHUNKS),    \
-                     dim3(kReduceThreads), 0, stream, a.tmp_out,                                              \
-                     a.max_logits, a.exp_sums, a.context_lens, a.num_q_heads, a.partition_size,             \
-                     a.max_num_partitions, a.out)
   if (a.bf16) {
-    if (a.head_dim == 64) PKA_REDUCE(BF16, 64);
-    else if (a.head_dim == 128) PKA_REDUCE(BF16, 128);
-    else if (a.head_dim == 256) PKA_REDUCE(BF16, 256);
-    else return hipErrorInvalidValue;
+    if (a.head_dim == 64) return launch_splitk_reduce_td<BF16, 64>(a, stream);
+    if (a.head_dim == 128) return launch_splitk_reduce_td<BF16, 128>(a, stream);
+    if (a.head_dim == 256) return launch_splitk_reduce_td<BF16, 256>(a, stream);
   } else {
-    if (a.head_dim == 64) PKA_REDUCE(F16, 64);
-    else if (a.head_dim == 128) PKA_REDUCE(F16, 128);
-    else if (a.head_dim == 256) PKA_REDUCE(F16, 256);
-    else return hipErrorInvalidValue;
+    if (a.head_dim == 64) return launch_splitk_reduce_td<F16, 64>(a, stream);
+    if (a.head_dim == 128) return launch_splitk_reduce_td<F16, 128>(a, stream);
+    if (a.head_dim == 256) return launch_splitk_reduce_td<F16, 256>(a, stream);
   }
-#undef PKA_REDUCE
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pka

@@ -1,0 +1,8 @@
+// Decode kernels for bf16 at head size 64 (one translation unit per
+// (element type, head size), so the instances compile in parallel).
+
+#include "decode_impl.h"
+
+namespace pka {
+PKA_DECODE_INSTANTIATE(BF16, 64)
+}  // namespace pka

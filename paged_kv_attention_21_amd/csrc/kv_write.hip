@@ -18,14 +18,16 @@ constexpr int kKvWriteThreads = 256;
 __global__ void __launch_bounds__(kKvWriteThreads)
 kv_cache_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
                       const int64_t* __restrict__ slot_mapping, int64_t total_pieces, int32_t row_pieces,
-                      uint4* __restrict__ k_cache, uint4* __restrict__ v_cache) {
+                      int64_t num_slots, uint4* __restrict__ k_cache, uint4* __restrict__ v_cache) {
   const int64_t idx = (int64_t)blockIdx.x * kKvWriteThreads + threadIdx.x;
   if (idx >= total_pieces) return;
   const int32_t per_token = 2 * row_pieces;
   const int64_t tok = idx / per_token;
   const int32_t piece = (int32_t)(idx - tok * per_token);
   const int64_t slot = slot_mapping[tok];
-  if (slot < 0) return;  // padded row
+  // Padded row; a slot past the pool (a broken precondition) is skipped too
+  // rather than written out of bounds.
+  if (slot < 0 || slot >= num_slots) return;
   if (piece < row_pieces) {
     k_cache[slot * row_pieces + piece] = key[tok * row_pieces + piece];
   } else {
@@ -41,7 +43,7 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_cache_write_kernel, dim3((unsigned)blocks), dim3(kKvWriteThreads), 0, stream,
                      static_cast<const uint4*>(a.key), static_cast<const uint4*>(a.value), a.slot_mapping, total,
-                     row_pieces, static_cast<uint4*>(a.k_cache), static_cast<uint4*>(a.v_cache));
+                     row_pieces, a.num_slots, static_cast<uint4*>(a.k_cache), static_cast<uint4*>(a.v_cache));
   return hipGetLastError();
 }
 

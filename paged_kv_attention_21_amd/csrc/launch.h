@@ -9,6 +9,20 @@ namespace pka {
 // Split-K partition length in tokens (one partition = 16 KV blocks).
 constexpr int kPartitionSize = 256;
 
+// The dispatched split-K decode runs as one launch: the partitions of each
+// (sequence, KV head) are counted as they finish, and the last one merges
+// them.  The counters sit in a fixed header at the start of the workspace
+// (so partial results of a call with other sizes never land on them); every
+// call leaves them at zero.  Batches with more (sequence, KV head) pairs than
+// the header holds take the two-launch path (partitions, then the reduce).
+constexpr int kSplitCounterSlots = 16384;
+constexpr size_t kSplitCounterBytes = kSplitCounterSlots * sizeof(uint32_t);
+
+// Launch forms of the decode kernels (see decode_impl.h).
+constexpr int kLaunchSingle = 0;
+constexpr int kLaunchSplit = 1;
+constexpr int kLaunchSplitFused = 2;
+
 // Keys per prefill split: a query tile that sees more keys is spread over
 // several workgroups whose states are merged afterwards.
 // Shortest key range a prefill split is given (four 64-key tiles), and the
@@ -37,6 +51,7 @@ struct DecodeArgs {
   float* tmp_out;    // split-K only
   float* max_logits;
   float* exp_sums;
+  uint32_t* counters;  // single-launch split-K: one per (sequence, KV head), zero before the launch
   // Appended token (pka_paged_attn_decode_append): rows [num_seqs][kv heads][D]
   // stored at position context_lens[s] - 1 and attended from registers; null otherwise.
   const uint16_t* new_k;
@@ -65,6 +80,7 @@ struct KvWriteArgs {
   const int64_t* slot_mapping;
   int32_t num_tokens;
   int32_t row_bytes;  // num_kv_heads * head_dim * element size, a multiple of 16
+  int64_t num_slots;  // num_blocks * block_size: slots at or past it are skipped like padding
   void* k_cache;
   void* v_cache;
 };
@@ -92,7 +108,7 @@ struct PrefillArgs {
   float* workspace;  // split states; may be null when no tile needs more than one split
 };
 
-hipError_t launch_decode(const DecodeArgs& a, bool split, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int mode, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceArgs& a, hipStream_t stream);
 struct RopeKvArgs {
   const uint16_t* qkv;       // [T, row_stride] rows: q heads, k heads, v heads
@@ -101,6 +117,8 @@ struct RopeKvArgs {
   const int64_t* slot_mapping;
   const float* table;        // [max_position][head_dim / 2] (cos, sin) pairs
   int32_t num_tokens, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_position;      // rows of the table; positions are clamped into [0, max_position)
+  int64_t num_slots;         // num_blocks * block_size: slots at or past it are skipped like padding
   bool bf16;
   uint16_t* q_out;           // [T, Hq, D]
   uint16_t* k_cache;

@@ -2,8 +2,8 @@
 //
 // mini_engine ("Roadmap") folds RoPE into the QKV split / KV-cache write, and
 // miniserve's "Engine" flowchart orders one layer as fused qkv projection,
-// RoPE, then the copy of the new K/V into the paged pool at
-// slot = block_id * block_size + offset.  One pass here reads the fused
+// RoPE, then the copy of each new token's K and V rows into its pool slot
+// (block_id * block_size + offset).  One pass here reads the fused
 // projection rows [q heads | k heads | v heads] once, writes the rotated q
 // heads to a contiguous q tensor, and scatters the rotated k heads and the
 // untouched v heads into their cache slots (negative slots are padding).
@@ -29,7 +29,8 @@ template <typename T>
 __global__ void __launch_bounds__(kRopeThreads)
 rope_kv_write_kernel(const uint16_t* __restrict__ qkv, int64_t row_stride, const int64_t* __restrict__ positions,
                      const int64_t* __restrict__ slot_mapping, const float* __restrict__ table, int64_t total,
-                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, uint16_t* __restrict__ q_out,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_position,
+                     int64_t num_slots, uint16_t* __restrict__ q_out,
                      uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
   using E = Elem<T>;
   const int64_t idx = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
@@ -51,7 +52,9 @@ rope_kv_write_kernel(const uint16_t* __restrict__ qkv, int64_t row_stride, const
   int64_t slot = 0;
   if (head >= num_q_heads) {
     slot = slot_mapping[tok];
-    if (slot < 0) return;  // padded token: nothing goes to the cache
+    // Padded token: nothing goes to the cache (nor for a slot past the pool,
+    // a broken precondition).
+    if (slot < 0 || slot >= num_slots) return;
   }
   const int64_t kv_row = (int64_t)num_kv_heads * head_dim;  // elements per cache row (slot)
   if (is_v) {
@@ -61,8 +64,10 @@ rope_kv_write_kernel(const uint16_t* __restrict__ qkv, int64_t row_stride, const
     return;
   }
 
-  // (cos, sin) pairs of elements e0 .. e0 + 7 at this token's position.
-  const float4* cs = reinterpret_cast<const float4*>(table + (positions[tok] * half + e0) * 2);
+  // (cos, sin) pairs of elements e0 .. e0 + 7 at this token's position (a
+  // position outside the table, a broken precondition, is clamped into it).
+  const int64_t pos = min(max(positions[tok], (int64_t)0), (int64_t)max_position - 1);
+  const float4* cs = reinterpret_cast<const float4*>(table + (pos * half + e0) * 2);
   float c[8], s[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -123,11 +128,11 @@ hipError_t launch_rope_kv_write(const RopeKvArgs& a, hipStream_t stream) {
   if (a.bf16)
     hipLaunchKernelGGL(rope_kv_write_kernel<BF16>, dim3((unsigned)blocks), dim3(kRopeThreads), 0, stream, a.qkv,
                        a.row_stride, a.positions, a.slot_mapping, a.table, total, a.num_q_heads, a.num_kv_heads,
-                       a.head_dim, a.q_out, a.k_cache, a.v_cache);
+                       a.head_dim, a.max_position, a.num_slots, a.q_out, a.k_cache, a.v_cache);
   else
     hipLaunchKernelGGL(rope_kv_write_kernel<F16>, dim3((unsigned)blocks), dim3(kRopeThreads), 0, stream, a.qkv,
                        a.row_stride, a.positions, a.slot_mapping, a.table, total, a.num_q_heads, a.num_kv_heads,
-                       a.head_dim, a.q_out, a.k_cache, a.v_cache);
+                       a.head_dim, a.max_position, a.num_slots, a.q_out, a.k_cache, a.v_cache);
   return hipGetLastError();
 }
 

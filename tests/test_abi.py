@@ -159,9 +159,11 @@ def test_prefill_split_policy(pka, shape):
 
 
 def test_workspace_bytes_and_dispatcher(pka):
-    # config-4 shape: 4 seqs x 16 heads x 64 partitions x 128 dims fp32, plus max/sum arrays
+    # config-4 shape: the 64 KiB header of arrival counters, then 4 seqs x 16 heads
+    # x 64 partitions x 128 dims fp32, plus max/sum arrays
     rows = 4 * 16 * 64
-    assert pka.splitk_workspace_bytes(4, 16, 128, 16384) == rows * 128 * 4 + 2 * ((rows * 4 + 255) // 256 * 256)
+    assert pka.splitk_workspace_bytes(4, 16, 128, 16384) == (65536 + rows * 128 * 4
+                                                             + 2 * ((rows * 4 + 255) // 256 * 256))
     assert pka.splitk_workspace_bytes(0, 16, 128, 100) == 0
     cv = pka.decode_choose_variant
     assert cv(1, 2, 128, 256) == 1            # one partition: nothing to split

@@ -162,7 +162,7 @@ def test_splitk_partition_state_matches_oracle(pka):
         assert em < 1e-4 and el < 1e-4 and eo < 1e-4
 
 
-@pytest.mark.parametrize("variant", ["v1", "v2"])
+@pytest.mark.parametrize("variant", ["v1", "v2", "auto"])
 def test_block_placement_bit_identity(pka, variant):
     """Relabelling physical blocks (moving contents and table entries
     together) must not change a single output bit: the summation order depends
@@ -257,3 +257,69 @@ def test_one_round_grid_pairing(pka, num_seqs, hkv):
     for variant in ("v1", "auto"):
         out = run_decode(pka, ds, variant)
         assert_parity(out, oracle_decode(step), step.dtype, f"pairing {num_seqs}x{hkv} {variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_fp16_long_context_reduce_loop(pka, variant):
+    """fp16 (tolerance 2e-3) at 6,400+ tokens: 26-40 partitions per sequence,
+    so the reduce's unrolled partition loop and the single-launch merge run
+    at the tighter fp16 bound, next to shorter sequences of the same batch."""
+    step = W.make_decode_step(context_lens=[6401, 10240, 777, 7000], dtype=torch.float16, num_q_heads=8,
+                              num_kv_heads=4, head_dim=128, seed=12, poison=True)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), step.dtype, f"fp16 6,400+ tokens {variant}")
+
+
+@pytest.mark.parametrize("variant", ["v2", "auto"])
+@pytest.mark.parametrize("shape", [(torch.float16, 2, 2, 64, 262400), (torch.bfloat16, 16, 8, 128, 140000)],
+                         ids=["fp16-2q2kv-d64-262400", "bf16-16q8kv-d128-140000"])
+def test_more_partitions_than_one_merge_pass(pka, shape, variant):
+    """Contexts whose partitions exceed one pass of the merge: 1,025
+    partitions (the reduce stages 1,024 per pass; the single-launch merge
+    1,024 / G per pass) and 547 partitions at G = 2 (two merge passes), with
+    a short sequence beside the long one."""
+    dtype, hq, hkv, d, ctx = shape
+    step = W.make_decode_step(context_lens=[ctx, 300], dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                              seed=13, poison=True, pool_factor=1.02)
+    ds = DevStep(step)
+    out = run_decode(pka, ds, variant)
+    assert_parity(out, oracle_decode(step), dtype, f"{ctx} tokens {variant}")
+
+
+def test_single_launch_splitk_workspace_reuse(pka):
+    """The single-launch split-K leaves its arrival counters at zero: one
+    workspace (zeroed once) serves calls of different sizes in a row, its
+    partial-result region filled with garbage before each, and the counter
+    header reads zero after every call."""
+    ws = pka.splitk_workspace(8, 16, 128, 9000, "cuda")
+    header = 65536
+    cases = [([9000, 4000, 300, 8192], 8), ([5000], 1), ([7000, 6000, 1, 256, 257, 4097, 8999, 2000], 8),
+             ([3000, 9000], 2)]
+    for i, (ctx, n) in enumerate(cases):
+        step = W.make_decode_step(context_lens=ctx, dtype=torch.bfloat16, num_q_heads=16, num_kv_heads=8,
+                                  head_dim=128, seed=20 + i, poison=True)
+        ds = DevStep(step)
+        assert pka.decode_choose_variant(n, 8, max(ctx)) == 2
+        ws[header:].fill_(0xFF)
+        say(f"workspace reuse call {i}: contexts {ctx}")
+        out = pka.paged_attn_decode(ds.decode_q, ds.k_cache, ds.v_cache, ds.decode_block_tables,
+                                    ds.decode_context_lens, step.scale, max(ctx), workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out, oracle_decode(step), step.dtype, f"workspace reuse call {i}")
+        assert int(ws[:header].count_nonzero()) == 0, f"call {i} left a counter non-zero"
+
+
+def test_splitk_two_launch_fallback_many_pairs(pka):
+    """More (sequence, KV head) pairs than the counter header holds (2,100 x
+    8 > 16,384) with a context long enough for split-K: the dispatcher takes
+    the partition pass + reduce in two launches."""
+    g = torch.Generator().manual_seed(2100)
+    ctx = torch.randint(1, 400, (2100,), generator=g)
+    ctx[::300] = 4600
+    step = W.make_decode_step(context_lens=ctx.tolist(), dtype=torch.bfloat16, num_q_heads=8, num_kv_heads=8,
+                              head_dim=64, seed=14, poison=True)
+    assert pka.decode_choose_variant(2100, 8, int(ctx.max())) == 2
+    ds = DevStep(step)
+    out = run_decode(pka, ds, "auto")
+    assert_parity(out, oracle_decode(step), step.dtype, "2,100 x 8 pairs, two-launch split-K")

@@ -60,7 +60,7 @@ def test_ragged_chunks(pka, shape):
                                head_dim=d, seed=31, poison=True, write_new=False)
     ds = DevStep(step)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step), dtype, f"ragged prefill {shape}")
+    assert_parity(out, oracle_prefill(step), dtype, f"ragged prefill {shape}", weights_rounded=True)
 
 
 @pytest.mark.parametrize("shape", [(torch.bfloat16, 16, 8, 128), (torch.float16, 8, 8, 64)],
@@ -84,7 +84,7 @@ def test_long_context_splits(pka, shape):
                                write_new=False)
     ds = DevStep(step)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step), dtype, f"long-context splits {shape}")
+    assert_parity(out, oracle_prefill(step), dtype, f"long-context splits {shape}", weights_rounded=True)
 
 
 def test_workspace_reuse_across_calls(pka):
@@ -104,7 +104,7 @@ def test_workspace_reuse_across_calls(pka):
                                      ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len, mcl,
                                      workspace=ws)
         torch.cuda.synchronize()
-        assert_parity(out, ref, step.dtype, f"reused workspace call {call}")
+        assert_parity(out, ref, step.dtype, f"reused workspace call {call}", weights_rounded=True)
         outs.append(out.cpu().view(torch.int16))
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
@@ -118,7 +118,7 @@ def test_shared_prefix_chunks(pka):
     assert step.refcount.max() == 3
     ds = DevStep(step)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step), step.dtype, "shared-prefix prefill")
+    assert_parity(out, oracle_prefill(step), step.dtype, "shared-prefix prefill", weights_rounded=True)
 
 
 def test_write_then_prefill(pka):
@@ -129,7 +129,7 @@ def test_write_then_prefill(pka):
     pka.kv_cache_write(ds.new_k, ds.new_v, ds.slot_mapping, ds.k_cache, ds.v_cache)
     kc, vc = oracle.kv_cache_write(step.new_k, step.new_v, step.slot_mapping, step.k_cache, step.v_cache)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step, kc, vc), step.dtype, "write then prefill")
+    assert_parity(out, oracle_prefill(step, kc, vc), step.dtype, "write then prefill", weights_rounded=True)
 
 
 @pytest.mark.parametrize("seed", [0, 1])
@@ -154,7 +154,7 @@ def test_config5_mixed_step_full(pka, seed):
     ref_dec = oracle.decode(step.decode_q, kc, vc, step.decode_block_tables, step.decode_context_lens, step.scale)
     assert_parity(out[:nd], ref_dec, step.dtype, f"config5 seed {seed} decode rows")
     ref_pre = oracle_prefill(step, kc, vc)
-    assert_parity(out[nd:], ref_pre, step.dtype, f"config5 seed {seed} prefill rows")
+    assert_parity(out[nd:], ref_pre, step.dtype, f"config5 seed {seed} prefill rows", weights_rounded=True)
 
 
 def test_single_row_chunk_matches_decode_rows(pka):
@@ -164,7 +164,7 @@ def test_single_row_chunk_matches_decode_rows(pka):
     ds = DevStep(step)
     out = run_prefill(pka, ds)
     ref = oracle.decode(step.q, step.k_cache, step.v_cache, step.block_tables, step.context_lens, step.scale)
-    assert_parity(out, ref, step.dtype, "one-row chunks vs decode oracle")
+    assert_parity(out, ref, step.dtype, "one-row chunks vs decode oracle", weights_rounded=True)
     dec = pka.paged_attn_decode_v1(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.context_lens, step.scale)
     torch.cuda.synchronize()
     assert_parity(dec, ref, step.dtype, "decode kernel on the same rows")
@@ -209,7 +209,7 @@ def test_general_shapes(pka, shape):
                                poison=True, write_new=False)
     ds = DevStep(step)
     out = run_prefill(pka, ds)
-    assert_parity(out, oracle_prefill(step), dtype, f"prefill shape {shape}")
+    assert_parity(out, oracle_prefill(step), dtype, f"prefill shape {shape}", weights_rounded=True)
 
 
 def test_long_prefill_bench_size_sampled_rows(pka):
@@ -239,4 +239,5 @@ def test_long_prefill_bench_size_sampled_rows(pka):
         rows.update((b + torch.randint(0, 2048, (6,), generator=g)).tolist())
     rows = sorted(rows)
     ref = oracle_prefill(step, rows=rows)
-    assert_parity(out.cpu()[rows], ref[rows], step.dtype, f"long prefill bench size, {len(rows)} sampled rows")
+    assert_parity(out.cpu()[rows], ref[rows], step.dtype, f"long prefill bench size, {len(rows)} sampled rows",
+                  weights_rounded=True)

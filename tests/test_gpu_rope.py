@@ -4,14 +4,13 @@ spacing (the kernel rotates in fp32 and rounds once, the oracle in fp64):
 at most one unit apart, and most of them identical; V and every byte of the
 pool outside the written slots must be bit-exact."""
 
-import math
 
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import say
+from tests.gpu_util import assert_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -154,6 +153,8 @@ def test_rotated_write_then_decode(pka):
     ref_q, ref_k, ref_v = oracle.fused_rope_kv_write(qkv, step.positions, step.slot_mapping, step.k_cache,
                                                      step.v_cache, 16, 8, THETA)
     ref = oracle.decode(ref_q, ref_k, ref_v, step.block_tables, step.context_lens, step.scale)
-    err = (out.cpu().double() - ref).abs().max().item()
-    say(f"rotate-write-decode max abs err {err:.3e}")
-    assert err <= 1.5e-2 and not math.isnan(err)
+    # q and k come from the GPU's own rounding of the rotation (within one unit
+    # of the output spacing of the oracle's), so the decode sees inputs that
+    # differ from the oracle's by up to one ulp: the looser of the two scaled
+    # bounds (one input rounding per term) applies.
+    assert_parity(out, ref, torch.bfloat16, "rotate-write-decode", weights_rounded=True)

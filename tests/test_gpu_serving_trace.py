@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import TOL, say
+from tests.gpu_util import assert_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -112,10 +112,8 @@ class Trace:
         return out, oracle.decode(q, tk, tv, bt, cl, SCALE)
 
 
-def _check(out, ref, what):
-    err = (out.cpu().double() - ref).abs().max().item()
-    say(f"{what}: max abs err {err:.3e}")
-    assert err <= TOL[DT], f"{what}: {err}"
+def _check(out, ref, what, weights_rounded=False):
+    assert_parity(out, ref, DT, what, weights_rounded=weights_rounded)
 
 
 def test_serving_trace_with_prefix_reuse(pka):
@@ -144,7 +142,7 @@ def test_serving_trace_with_prefix_reuse(pka):
         if wave > 0:
             assert hits > 0, "shared prefixes should hit the cache after the first wave"
         out, ref = tr.prefill(batch, starts)
-        _check(out, ref, f"wave {wave} prefill")
+        _check(out, ref, f"wave {wave} prefill", weights_rounded=True)
         live += batch
         for step in range(3):
             out, ref = tr.decode(live)
