@@ -46,6 +46,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace pka {
@@ -128,30 +129,30 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge, in the workgroup whose partition arrived last, the P partition
-// states of query heads kvh*G .. kvh*G+G-1 of one sequence, with the same
-// max / exp-sum rule as the split-K reduce: M = max_p m_p,
-// w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p.  Partitions go in
-// passes of kMergeEntries / G: their max logits and exp-sums are staged in
-// LDS, one wavefront per head forms the pass max and the weights (a running
-// max rescales earlier passes), then each thread accumulates w_p o_p for one
-// 4-dim column over every PP-th partition - all of its loads independent, so
-// they are in flight together - and the PP partition groups are summed
-// through LDS.
-constexpr int kMergeEntries = 1024;  // (head, partition) pairs staged per pass
-
+// Merge, in the workgroup that arrived last, the P states of query heads
+// kvh*G .. kvh*G+G-1 of one sequence (row stride `rows` in the workspace),
+// with the same max / exp-sum rule as the split-K reduce: M = max_p m_p,
+// w_p = l_p exp(m_p - M), out = sum_p w_p o_p / sum_p w_p.  Each thread owns
+// CPT 4-dim columns over the group's heads and every PP-th state (PP groups
+// of threads per column).  States go in passes of CH: a pass first issues the
+// thread's o loads into registers (they do not depend on the weights), then
+// stages the pass's max logits and exp-sums in LDS, where one wavefront per
+// head forms the pass max and the weights (a running max rescales earlier
+// passes) - so a pass costs one round trip to memory.  The PP groups are
+// summed through LDS at the end.
 template <typename T, int D, int G, int W>
 __device__ __forceinline__ void merge_group_partitions(const float* __restrict__ tmp_out,
                                                        const float* __restrict__ max_logits,
                                                        const float* __restrict__ exp_sums, int seq, int kvh,
-                                                       int num_q_heads, int max_num_partitions, int P,
+                                                       int num_q_heads, int rows, int P,
                                                        uint16_t* __restrict__ out) {
   typedef float float4v_t __attribute__((ext_vector_type(4)));
   constexpr int NT = W * kWave;
   constexpr int COLS = G * D / 4;                // 4-dim columns over the group's heads
   constexpr int CPT = COLS > NT ? COLS / NT : 1;  // columns per thread
   constexpr int PP = COLS >= NT ? 1 : NT / COLS;  // partition groups
-  constexpr int CH = kMergeEntries / G;           // partitions per pass
+  constexpr int VPT = 8;                          // o vectors per column and pass, per thread
+  constexpr int CH = VPT * PP;                    // states per pass
   static_assert(COLS % NT == 0 || NT % COLS == 0, "whole columns per thread");
   __shared__ float s_w[G][CH], s_l[G][CH];
   __shared__ float s_run[3][G];  // running max, running weight sum, this pass's rescale
@@ -159,7 +160,8 @@ __device__ __forceinline__ void merge_group_partitions(const float* __restrict__
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = wave_id();
-  const size_t row0 = ((size_t)seq * num_q_heads + (size_t)kvh * G) * max_num_partitions;  // head g: + g * max P
+  const int pg = PP > 1 ? tid / COLS : 0;
+  const size_t row0 = ((size_t)seq * num_q_heads + (size_t)kvh * G) * rows;  // head g: + g * rows
   float4v_t acc[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) acc[c] = float4v_t{0.f, 0.f, 0.f, 0.f};
@@ -169,9 +171,27 @@ __device__ __forceinline__ void merge_group_partitions(const float* __restrict__
   }
   for (int p0 = 0; p0 < P; p0 += CH) {
     const int n = min(CH, P - p0);
+    // This thread's o vectors of the pass (states pg, pg + PP, ...).
+    float4v_t ov[CPT][VPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int col = PP > 1 ? tid % COLS : tid + c * NT;
+      const int g = col / (D / 4), d4 = col % (D / 4);
+      const float* po = tmp_out + (row0 + (size_t)g * rows + p0) * D + 4 * d4;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const int p = pg + v * PP;
+        ov[c][v] = float4v_t{0.f, 0.f, 0.f, 0.f};
+        if (p < n) {
+          const float* src = po + (size_t)p * D;
+          ov[c][v] = float4v_t{load_coherent(src), load_coherent(src + 1), load_coherent(src + 2),
+                               load_coherent(src + 3)};
+        }
+      }
+    }
     for (int i = tid; i < G * n; i += NT) {
       const int g = i / n, p = i - g * n;
-      const size_t idx = row0 + (size_t)g * max_num_partitions + p0 + p;
+      const size_t idx = row0 + (size_t)g * rows + p0 + p;
       s_w[g][p] = load_coherent(max_logits + idx);
       s_l[g][p] = load_coherent(exp_sums + idx);
     }
@@ -202,15 +222,12 @@ __device__ __forceinline__ void merge_group_partitions(const float* __restrict__
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int col = PP > 1 ? tid % COLS : tid + c * NT;
-      const int pg = PP > 1 ? tid / COLS : 0;
-      const int g = col / (D / 4), d4 = col % (D / 4);
+      const int g = col / (D / 4);
       acc[c] *= s_run[2][g];
-      const float* po = tmp_out + (row0 + (size_t)g * max_num_partitions + p0) * D + 4 * d4;
-#pragma unroll 8
-      for (int p = pg; p < n; p += PP) {
-        const float* src = po + (size_t)p * D;
-        const float4v_t v = {load_coherent(src), load_coherent(src + 1), load_coherent(src + 2), load_coherent(src + 3)};
-        acc[c] += s_w[g][p] * v;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const int p = pg + v * PP;
+        if (p < n) acc[c] += s_w[g][p] * ov[c][v];
       }
     }
     __syncthreads();  // s_w and s_l are rewritten by the next pass
@@ -220,7 +237,7 @@ __device__ __forceinline__ void merge_group_partitions(const float* __restrict__
     __syncthreads();
     if (tid >= COLS) return;
 #pragma unroll
-    for (int pg = 1; pg < PP; ++pg) acc[0] += s_red[pg * COLS + tid];
+    for (int q = 1; q < PP; ++q) acc[0] += s_red[q * COLS + tid];
   }
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -241,6 +258,16 @@ enum DecodeMode : int {
 };
 
 // BS = tokens per KV block (8, 16 or 32).
+//
+// Single pass and split-K partition pass: the workgroup's range is the
+// sequence (or one 256-token partition of it) and its W wavefronts take the
+// range's blocks round-robin; the wavefronts' states are merged through LDS.
+// Single-launch split-K (MODE kDecodeSplitFused): grid (KV head, Y, sequence);
+// each wavefront takes whole 256-token partitions, wavefront w of workgroup y
+// partitions y*W + w, y*W + w + Y*W, ..., streaming each partition's blocks on
+// its own; the workgroup merges its wavefronts' states through LDS, publishes
+// the result as one state (row y of the workspace), and the last of the
+// sequence's workgroups to arrive merges those states into the output.
 template <typename T, int D, int G, int W, int MODE, int BS>
 __global__ void __launch_bounds__(W * kWave)
 paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -253,13 +280,14 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     uint16_t* __restrict__ k_store, uint16_t* __restrict__ v_store, int32_t pair_from,
                     uint32_t* __restrict__ counters) {
   constexpr bool SPLIT = MODE != kDecodeSingle;
+  constexpr bool FUSED = MODE == kDecodeSplitFused;
   using L = DecodeLayout<D, BS>;
   constexpr int kBlockSize = BS;
   using E = Elem<T>;
   constexpr int LPT = L::LPT, TPL = L::TPL, LPB = L::LPB;
 
   const int kvh = blockIdx.x;
-  const int part = SPLIT ? (int)blockIdx.y : 0;
+  const int part = MODE == kDecodeSplit ? (int)blockIdx.y : 0;
   int seq = SPLIT ? (int)blockIdx.z : (int)blockIdx.y;
   if constexpr (!SPLIT) {
     __shared__ int order_lds[kOrderBuckets + 1];
@@ -273,22 +301,26 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int num_q_heads = num_kv_heads * G;
 
   const int ctx = context_lens[seq];
-  int tok_begin = 0, tok_end = ctx;
-  if constexpr (SPLIT) {
-    tok_begin = part * kPartitionSize;
-    if (tok_begin >= ctx) {  // past this sequence's end: nothing to write
-      if (MODE == kDecodeSplitFused && ctx <= 0 && part == 0) {
+  // Single-launch split-K: the sequence's partitions (at most one row of the
+  // host-sized workspace each) and the workgroups that hold some of them.
+  const int num_parts = FUSED ? min((max(ctx, 0) + kPartitionSize - 1) / kPartitionSize, max_num_partitions) : 0;
+  const int wg_active = FUSED ? min((int)gridDim.y, (num_parts + W - 1) / W) : 0;
+  if constexpr (FUSED) {
+    if ((int)blockIdx.y >= wg_active) {  // no partition for this workgroup
+      if (ctx <= 0 && blockIdx.y == 0) {
         // An empty context has no partition to merge: its output is 0.
         for (int t = threadIdx.x; t < G * D; t += W * kWave)
-          out[((size_t)seq * num_kv_heads * G + (size_t)kvh * G + t / D) * D + t % D] = 0;
+          out[((size_t)seq * num_q_heads + (size_t)kvh * G + t / D) * D + t % D] = 0;
       }
       return;
     }
+  }
+  int tok_begin = 0, tok_end = ctx;
+  if constexpr (MODE == kDecodeSplit) {
+    tok_begin = part * kPartitionSize;
+    if (tok_begin >= ctx) return;  // past this sequence's end: nothing to write
     tok_end = min(ctx, tok_begin + kPartitionSize);
   }
-  const int lb_begin = tok_begin / kBlockSize;
-  const int nblk = tok_end > tok_begin ? (tok_end - tok_begin + kBlockSize - 1) / kBlockSize : 0;
-  const int last_valid = tok_end - (lb_begin + nblk - 1) * kBlockSize;  // tokens in the range's last block
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_id();
@@ -302,9 +334,8 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // cached copy may be stale or NaN until then: it is loaded and selected
   // out, never read back) and stores the row to its slot, whose block it
   // already holds, so no extra table lookup delays the start of the loop.
-  const bool append = new_k != nullptr && ctx > 0 && tok_end == ctx;
   uint4 app_k = make_uint4(0, 0, 0, 0), app_v = app_k;
-  if (append) {
+  if (new_k != nullptr && ctx > 0 && (FUSED || tok_end == ctx)) {
     const size_t src = ((size_t)seq * num_kv_heads + kvh) * D + col * 8;
     app_k = *reinterpret_cast<const uint4*>(new_k + src);
     app_v = *reinterpret_cast<const uint4*>(new_v + src);
@@ -335,10 +366,19 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   for (int i = 0; i < LPB; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
   const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
   const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
-  const int32_t* tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
 
-  // This wavefront's blocks are wave, wave + W, wave + 2W, ... (< nblk).
-  const int nb_wave = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+  // The range being streamed: its blocks, the tokens in its last block, and
+  // whether it ends with the appended token.
+  int nblk = 0, last_valid = 0;
+  bool append = false;
+  const int32_t* tbl = block_tables;
+  auto set_range = [&](int b, int e) {
+    const int lb_begin = b / kBlockSize;
+    nblk = e > b ? (e - b + kBlockSize - 1) / kBlockSize : 0;
+    last_valid = e - (lb_begin + nblk - 1) * kBlockSize;
+    append = new_k != nullptr && ctx > 0 && e == ctx;
+    tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
+  };
 
   auto issue = [&](int pb, uint4 (&kk)[LPB], uint4 (&vv)[LPB]) {
     const char* kb = kbase + (size_t)pb * block_bytes;
@@ -435,31 +475,47 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // Main loop, double-buffered over this wavefront's blocks: while a block is
-  // consumed the next one's 2*LPB loads are in flight.  The steady-state body
-  // issues unconditionally, so every consume in it waits for its own loads
-  // only; the 1-3 blocks left at the end of a window are peeled (their waits
-  // may be conservative, and no block is fetched twice).  Table entries come
-  // 64 at a time (lane k holds the entry of the wave's block j0 + k).
-  uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
-  for (int j0 = 0; j0 < nb_wave; j0 += kWave) {
-    const int jn = min(kWave, nb_wave - j0);
-    const int tbl_win = lane < jn ? tbl[wave + (j0 + lane) * W] : 0;
-    const int blk_base = wave + j0 * W;  // range-relative index of the window's block 0
-    issue(uniform_lane(tbl_win, 0), ka, va);
-    if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
-    int j = 0;
-    for (; j + 3 < jn; j += 2) {
-      consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
-      issue(uniform_lane(tbl_win, j + 2), ka, va);
-      consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
-      issue(uniform_lane(tbl_win, j + 3), kb2, vb2);
+  // Stream blocks first, first + stride, ... (< nblk) of the range: double
+  // buffered, so while a block is consumed the next one's 2*LPB loads are in
+  // flight.  The steady-state body issues unconditionally, so every consume
+  // in it waits for its own loads only; the 1-3 blocks left at the end of a
+  // window are peeled (their waits may be conservative, and no block is
+  // fetched twice).  Table entries come 64 at a time (lane k holds the entry
+  // of the wave's block j0 + k).
+  auto stream_blocks = [&](int first, int stride) {
+    const int nb = first < nblk ? (nblk - first + stride - 1) / stride : 0;
+    uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
+    for (int j0 = 0; j0 < nb; j0 += kWave) {
+      const int jn = min(kWave, nb - j0);
+      const int tbl_win = lane < jn ? tbl[first + (j0 + lane) * stride] : 0;
+      const int blk_base = first + j0 * stride;  // range-relative index of the window's block 0
+      issue(uniform_lane(tbl_win, 0), ka, va);
+      if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
+      int j = 0;
+      for (; j + 3 < jn; j += 2) {
+        consume(ka, va, blk_base + j * stride, uniform_lane(tbl_win, j));
+        issue(uniform_lane(tbl_win, j + 2), ka, va);
+        consume(kb2, vb2, blk_base + (j + 1) * stride, uniform_lane(tbl_win, j + 1));
+        issue(uniform_lane(tbl_win, j + 3), kb2, vb2);
+      }
+      const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
+      consume(ka, va, blk_base + j * stride, uniform_lane(tbl_win, j));
+      if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
+      if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * stride, uniform_lane(tbl_win, j + 1));
+      if (rem == 3) consume(ka, va, blk_base + (j + 2) * stride, uniform_lane(tbl_win, j + 2));
     }
-    const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
-    consume(ka, va, blk_base + j * W, uniform_lane(tbl_win, j));
-    if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
-    if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * W, uniform_lane(tbl_win, j + 1));
-    if (rem == 3) consume(ka, va, blk_base + (j + 2) * W, uniform_lane(tbl_win, j + 2));
+  };
+
+  if constexpr (FUSED) {
+    // This wavefront's partitions, one running state over all of them.
+    const int wstride = (int)gridDim.y * W;
+    for (int p = (int)blockIdx.y * W + wave; p < num_parts; p += wstride) {
+      set_range(p * kPartitionSize, min(ctx, (p + 1) * kPartitionSize));
+      stream_blocks(0, 1);
+    }
+  } else {
+    set_range(tok_begin, tok_end);
+    stream_blocks(wave, W);
   }
 
   // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
@@ -510,8 +566,9 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
     const int h = kvh * G + g;
     const float o = lt > 0.f ? at / lt : 0.f;
-    if constexpr (MODE == kDecodeSplitFused) {
-      const size_t idx = ((size_t)seq * num_q_heads + h) * max_num_partitions + part;
+    if constexpr (FUSED) {
+      // The workgroup's state: row blockIdx.y of the (sequence, head).
+      const size_t idx = ((size_t)seq * num_q_heads + h) * max_num_partitions + blockIdx.y;
       store_coherent(tmp_out + idx * D + d, o);
       if (d == 0) {
         store_coherent(max_logits + idx, mm * kLn2);  // back to natural-log units
@@ -529,25 +586,24 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   }
 
-  if constexpr (MODE == kDecodeSplitFused) {
-    // Publish this partition's state: every wavefront waits until its
-    // coherent stores have completed, then one thread counts the partition.
-    // The counter wraps to 0 on the last arrival, so every call leaves the
+  if constexpr (FUSED) {
+    // Publish the workgroup's state: every wavefront waits until its coherent
+    // stores have completed, then one thread counts the workgroup.  The
+    // counter wraps to 0 on the last arrival, so every call leaves the
     // counters as it found them; the workgroup that sees the wrap merges the
-    // sequence's partitions (reading them with coherent loads).
+    // sequence's workgroup states (reading them with coherent loads).
     __shared__ int s_last;
-    const int P = min((ctx + kPartitionSize - 1) / kPartitionSize, max_num_partitions);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
       const uint32_t prev = __builtin_amdgcn_atomic_inc32(counters + (size_t)seq * num_kv_heads + kvh,
-                                                          (uint32_t)(P - 1), __ATOMIC_RELAXED, "agent");
-      s_last = prev == (uint32_t)(P - 1);
+                                                          (uint32_t)(wg_active - 1), __ATOMIC_RELAXED, "agent");
+      s_last = prev == (uint32_t)(wg_active - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    merge_group_partitions<T, D, G, W>(tmp_out, max_logits, exp_sums, seq, kvh, num_q_heads, max_num_partitions, P,
-                                       out);
+    merge_group_partitions<T, D, G, W>(tmp_out, max_logits, exp_sums, seq, kvh, num_q_heads, max_num_partitions,
+                                       wg_active, out);
   }
 }
 
@@ -696,7 +752,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int mode, hipStream_t str
                        a.max_logits, a.exp_sums, a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store, 0,
                        nullptr);
   } else {
-    dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
+    // Single launch: enough workgroups per (sequence, KV head) that every
+    // wavefront of one resident round (two workgroups per compute unit) has a
+    // partition, and no more than the partitions need.
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t slots = 2 * (int64_t)(a.num_cus > 0 ? a.num_cus : 256);
+    const int64_t by_parts = (a.max_num_partitions + kSplitWaves - 1) / kSplitWaves;
+    const int y = (int)std::max<int64_t>(1, std::min<int64_t>(by_parts, slots / pairs));
+    dim3 grid(a.num_kv_heads, y, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, kDecodeSplitFused, BS>), grid,
                        dim3(kSplitWaves * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.num_kv_heads, scale_log2, a.out, a.tmp_out,

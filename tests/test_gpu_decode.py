@@ -272,19 +272,25 @@ def test_fp16_long_context_reduce_loop(pka, variant):
 
 
 @pytest.mark.parametrize("variant", ["v2", "auto"])
-@pytest.mark.parametrize("shape", [(torch.float16, 2, 2, 64, 262400), (torch.bfloat16, 16, 8, 128, 140000)],
-                         ids=["fp16-2q2kv-d64-262400", "bf16-16q8kv-d128-140000"])
+@pytest.mark.parametrize("shape", [(torch.float16, 2, 2, 64, [262400, 300]),
+                                   (torch.bfloat16, 16, 8, 128, [140000, 300]),
+                                   (torch.bfloat16, 16, 8, 128, [70000]),
+                                   (torch.bfloat16, 16, 2, 128, [9000])],
+                         ids=["fp16-2q2kv-d64-262400", "bf16-16q8kv-d128-140000", "bf16-16q8kv-d128-70000",
+                              "bf16-16q2kv-d128-9000"])
 def test_more_partitions_than_one_merge_pass(pka, shape, variant):
-    """Contexts whose partitions exceed one pass of the merge: 1,025
-    partitions (the reduce stages 1,024 per pass; the single-launch merge
-    1,024 / G per pass) and 547 partitions at G = 2 (two merge passes), with
-    a short sequence beside the long one."""
+    """Long contexts.  The two-launch reduce stages 1,024 partitions per
+    pass, so 1,025 partitions (262,400 tokens) take two.  The single-launch
+    path merges one state per workgroup in passes of 8 x (threads per
+    column) states: a lone 70,000-token sequence gives 64 workgroup states
+    (two passes of 32 at G = 2), and 9,000 tokens at G = 8 give 9 (two passes
+    of 8).  Short sequences ride beside the long ones."""
     dtype, hq, hkv, d, ctx = shape
-    step = W.make_decode_step(context_lens=[ctx, 300], dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+    step = W.make_decode_step(context_lens=ctx, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                               seed=13, poison=True, pool_factor=1.02)
     ds = DevStep(step)
     out = run_decode(pka, ds, variant)
-    assert_parity(out, oracle_decode(step), dtype, f"{ctx} tokens {variant}")
+    assert_parity(out, oracle_decode(step), dtype, f"{ctx[0]} tokens {variant}")
 
 
 def test_single_launch_splitk_workspace_reuse(pka):
