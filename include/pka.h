@@ -77,7 +77,8 @@ typedef enum {
   PKA_ERR_UNSUPPORTED = 3, /* shape or dtype not built into the library */
   PKA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   PKA_ERR_WORKSPACE = 5,   /* split-K workspace missing or too small */
-  PKA_ERR_HIP = 6          /* the HIP runtime reported an error */
+  PKA_ERR_HIP = 6,         /* the HIP runtime reported an error */
+  PKA_ERR_SCRATCH = 7      /* pka_paged_attn_decode_noalloc: more than its scratch holds */
 } pka_status;
 
 /* Shape of one layer's paged KV pool (k_cache and v_cache alike). */
@@ -265,6 +266,30 @@ int32_t pka_paged_attn_decode_append(const void* q, const void* key, const void*
                                      int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
                                      void* out, pka_cache_desc cache, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free paged decode, for callers that cannot allocate device
+ * memory (code under HIP-graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same operation, arguments, dispatch and errors as
+ * pka_paged_attn_decode without the workspace: the split-K path uses an array
+ * inside the library instead, PKA_NOALLOC_SCRATCH_BYTES (32 MiB) per device,
+ * held by each device the library runs on until the process ends.  Returns
+ * PKA_ERR_SCRATCH, before launching anything, when the split-K path is chosen
+ * and pka_splitk_workspace_bytes(...) exceeds it (at head size 128 it holds
+ * about 64,000 (sequence, query head, partition) rows, e.g. 4 sequences of
+ * 256,000 tokens with 16 query heads).  Allocates nothing (no hipMalloc, no allocating library
+ * call); the first call on a device looks up the array's device address.  All
+ * calls on one device share the array: calls that overlap in time on one
+ * device (several streams or threads) race and must be serialised by the
+ * caller.  The array's arrival counters start at zero and every call leaves
+ * them at zero.
+ */
+#define PKA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+int32_t pka_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                      int32_t max_context_len, float scale, void* out, pka_cache_desc cache,
+                                      void* stream);
 
 /*
  * Paged prefill ([ME] paged prefill attention; [MS] bottom-right causal

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     kv_cache_write,
     paged_attn_decode,
     paged_attn_decode_append,
+    paged_attn_decode_noalloc,
     paged_attn_decode_splitk,
     paged_attn_decode_v1,
     paged_attn_prefill,

@@ -34,6 +34,7 @@ STATUS = {
     4: "PKA_ERR_ALIGN",
     5: "PKA_ERR_WORKSPACE",
     6: "PKA_ERR_HIP",
+    7: "PKA_ERR_SCRATCH",
 }
 
 
@@ -85,6 +86,11 @@ _SIGNATURES = {
         c_int32,
         [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
          c_float, c_void_p, CacheDesc, c_void_p, c_size_t, c_void_p],
+    ),
+    "pka_paged_attn_decode_noalloc": (
+        c_int32,
+        [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_void_p,
+         CacheDesc, c_void_p],
     ),
     "pka_paged_attn_prefill": (
         c_int32,
@@ -490,6 +496,21 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ma
                     block_tables.shape[1], int(max_context_len), float(scale), _ptr(out), cache_desc(k_cache),
                     _ptr(workspace), ws_bytes, _stream(q)),
                    prepare, (q, k_cache, v_cache, block_tables, context_lens, out, workspace), out)
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
+                              prepare=False):
+    """paged_attn_decode without a workspace: the split-K path uses the
+    library's own per-device scratch (nothing is allocated on any path when
+    `out` is given).  Calls that overlap on one device race on that scratch."""
+    _decode_common(q, k_cache, v_cache, block_tables, context_lens)
+    out = _out_like(q, out)
+    S, Hq, _ = q.shape
+    return _launch(lib.pka_paged_attn_decode_noalloc,
+                   (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), S, Hq,
+                    block_tables.shape[1], int(max_context_len), float(scale), _ptr(out), cache_desc(k_cache),
+                    _stream(q)),
+                   prepare, (q, k_cache, v_cache, block_tables, context_lens, out), out)
 
 
 def paged_attn_decode_append(q, key, value, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,

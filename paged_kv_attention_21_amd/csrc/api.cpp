@@ -11,8 +11,19 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "launch.h"
+
+// Library-owned scratch of the allocation-free decode entry point
+// (pka_paged_attn_decode_noalloc): the split-K counter header and partition
+// states live here instead of in a caller's workspace.  Every device the
+// library runs on holds its own copy until the process ends.  It starts
+// zeroed, so the counter header starts at zero, and every call leaves the
+// counters at zero.  Host code never passes the array's name to a kernel (on
+// the host it only stands in for the symbol): its device address is looked up
+// per device below.
+static __device__ __align__(256) unsigned char scratch[PKA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -44,6 +55,27 @@ int32_t check_group(int32_t num_q_heads, int32_t num_kv_heads, int32_t* group) {
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? PKA_OK : PKA_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKA_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKA_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKA_OK;
+}
 
 int32_t num_partitions(int32_t max_context_len) {
   return (max_context_len + pka::kPartitionSize - 1) / pka::kPartitionSize;
@@ -168,6 +200,7 @@ const char* pka_status_str(int32_t status) {
     case PKA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case PKA_ERR_WORKSPACE: return "split-K workspace missing or too small";
     case PKA_ERR_HIP: return "HIP runtime error";
+    case PKA_ERR_SCRATCH: return "request needs more split-K scratch than the library's built-in array holds";
   }
   return "unknown status";
 }
@@ -357,6 +390,28 @@ int32_t pka_paged_attn_decode_append(const void* q, const void* key, const void*
   if (num_seqs > 0 && (!aligned16(key) || !aligned16(value))) return PKA_ERR_ALIGN;
   return decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
                          max_context_len, scale, out, cache, workspace, workspace_bytes, stream, key, value);
+}
+
+int32_t pka_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, void* out, pka_cache_desc cache, void* stream) {
+  if (num_seqs < 0 || max_context_len < 0) return PKA_ERR_SHAPE;
+  if (num_seqs == 0) return PKA_OK;
+  if (max_context_len == 0 || cache.num_kv_heads <= 0) return PKA_ERR_SHAPE;
+  const int32_t variant = pka_decode_choose_variant(num_seqs, cache.num_kv_heads, max_context_len,
+                                                    pka_device_cu_count());
+  void* ws = nullptr;
+  if (variant == 2) {
+    if (pka_splitk_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len) >
+        (size_t)PKA_NOALLOC_SCRATCH_BYTES)
+      return PKA_ERR_SCRATCH;
+    const int32_t st = scratch_address(&ws);
+    if (st) return st;
+  }
+  return decode_dispatch(q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                         max_context_len, scale, out, cache, ws, ws ? (size_t)PKA_NOALLOC_SCRATCH_BYTES : 0, stream,
+                         nullptr, nullptr);
 }
 
 size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
