@@ -721,6 +721,17 @@ constexpr int kDecodeWaves = PKA_DECODE_WAVES;  // wavefronts per single-pass de
 #define PKA_SPLIT_WAVES 4
 #endif
 constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partition workgroup
+// Wavefronts per workgroup of the single-launch split-K.  Eight (one
+// workgroup per compute unit, half the workgroup states to merge) where the
+// kernel fits 256 registers per lane: measured on 4 x 16,384 tokens, 51.1
+// against 52.6 us per call with four.  Instances whose load buffers and
+// accumulators need more (16 registers per load of a block, 12 per query
+// head of the group, beyond ~100) would spill with eight and keep four, which
+// may use the accumulation registers as well.
+template <int D, int G, int BS>
+constexpr int fused_waves() {
+  return 16 * DecodeLayout<D, BS>::LPB + 12 * G <= 100 ? 8 : 4;
+}
 // Heavy-first ordering scans all context lengths in every workgroup; above
 // this many sequences the grid order is kept.
 constexpr int kOrderMaxSeqs = 1024;
@@ -753,15 +764,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int mode, hipStream_t str
                        nullptr);
   } else {
     // Single launch: enough workgroups per (sequence, KV head) that every
-    // wavefront of one resident round (two workgroups per compute unit) has a
+    // wavefront of one resident round (one workgroup per compute unit) has a
     // partition, and no more than the partitions need.
+    constexpr int FW = fused_waves<D, G, BS>();
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
-    const int64_t slots = 2 * (int64_t)(a.num_cus > 0 ? a.num_cus : 256);
-    const int64_t by_parts = (a.max_num_partitions + kSplitWaves - 1) / kSplitWaves;
+    const int64_t slots = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * (8 / FW);
+    const int64_t by_parts = (a.max_num_partitions + FW - 1) / FW;
     const int y = (int)std::max<int64_t>(1, std::min<int64_t>(by_parts, slots / pairs));
     dim3 grid(a.num_kv_heads, y, a.num_seqs);
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, kDecodeSplitFused, BS>), grid,
-                       dim3(kSplitWaves * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, G, FW, kDecodeSplitFused, BS>), grid,
+                       dim3(FW * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.num_kv_heads, scale_log2, a.out, a.tmp_out,
                        a.max_logits, a.exp_sums, a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store, 0,
                        a.counters);

@@ -274,17 +274,17 @@ def test_fp16_long_context_reduce_loop(pka, variant):
 @pytest.mark.parametrize("variant", ["v2", "auto"])
 @pytest.mark.parametrize("shape", [(torch.float16, 2, 2, 64, [262400, 300]),
                                    (torch.bfloat16, 16, 8, 128, [140000, 300]),
-                                   (torch.bfloat16, 16, 8, 128, [70000]),
-                                   (torch.bfloat16, 16, 2, 128, [9000])],
-                         ids=["fp16-2q2kv-d64-262400", "bf16-16q8kv-d128-140000", "bf16-16q8kv-d128-70000",
-                              "bf16-16q2kv-d128-9000"])
+                                   (torch.bfloat16, 4, 2, 128, [140000]),
+                                   (torch.bfloat16, 16, 2, 128, [40000])],
+                         ids=["fp16-2q2kv-d64-262400", "bf16-16q8kv-d128-140000", "bf16-4q2kv-d128-140000",
+                              "bf16-16q2kv-d128-40000"])
 def test_more_partitions_than_one_merge_pass(pka, shape, variant):
     """Long contexts.  The two-launch reduce stages 1,024 partitions per
     pass, so 1,025 partitions (262,400 tokens) take two.  The single-launch
-    path merges one state per workgroup in passes of 8 x (threads per
-    column) states: a lone 70,000-token sequence gives 64 workgroup states
-    (two passes of 32 at G = 2), and 9,000 tokens at G = 8 give 9 (two passes
-    of 8).  Short sequences ride beside the long ones."""
+    path merges one state per workgroup, 8 x (threads per 4-dim column) states
+    per pass: a lone 140,000-token sequence with 2 KV heads leaves 69
+    workgroup states at G = 2 (passes of 64), and 40,000 tokens at G = 8 leave
+    20 (passes of 16).  Short sequences ride beside the long ones."""
     dtype, hq, hkv, d, ctx = shape
     step = W.make_decode_step(context_lens=ctx, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                               seed=13, poison=True, pool_factor=1.02)
