@@ -137,6 +137,7 @@ int32_t decode_dispatch(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs > 65535) return PKA_ERR_UNSUPPORTED;
   a.out = static_cast<uint16_t*>(out);
   a.order_max_ctx = max_context_len;
+  a.max_context_len = max_context_len;
   if (new_k) {
     a.new_k = static_cast<const uint16_t*>(new_k);
     a.new_v = static_cast<const uint16_t*>(new_v);

@@ -278,7 +278,7 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     float* __restrict__ exp_sums, int32_t max_num_partitions, int32_t order_max_ctx,
                     const uint16_t* __restrict__ new_k, const uint16_t* __restrict__ new_v,
                     uint16_t* __restrict__ k_store, uint16_t* __restrict__ v_store, int32_t pair_from,
-                    uint32_t* __restrict__ counters) {
+                    uint32_t* __restrict__ counters, int32_t split_chunk) {
   constexpr bool SPLIT = MODE != kDecodeSingle;
   constexpr bool FUSED = MODE == kDecodeSplitFused;
   using L = DecodeLayout<D, BS>;
@@ -299,11 +299,29 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (order_max_ctx > 0) seq = heavy_first_seq<W * kWave>(context_lens, gridDim.y, order_max_ctx, seq, order_lds);
   }
   const int num_q_heads = num_kv_heads * G;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_id();
+
+  // The first 64 block-table entries this wavefront will stream (lane k: its
+  // k-th block), fetched before the context length is known so the two loads
+  // overlap instead of following each other.  The entries lie inside the
+  // sequence's table row; those past the context are never used.
+  // Single-launch split-K: each wavefront takes chunks of `chunk` tokens -
+  // the 256-token partition, or a power-of-two fraction of it (at least one
+  // KV block) when the device would otherwise be short of wavefronts; the
+  // host keeps the workgroup count within the workspace's rows.
+  const int chunk = FUSED ? split_chunk : kPartitionSize;
+  constexpr int kPartBlocks = kPartitionSize / BS;
+  const int pre_first = FUSED ? ((int)blockIdx.y * W + wave) * (chunk / BS)
+                              : (MODE == kDecodeSplit ? part * kPartBlocks : 0) + wave;
+  const int pre_idx = pre_first + lane * (FUSED ? 1 : W);
+  const int pre_win = pre_idx < max_blocks_per_seq ? block_tables[(size_t)seq * max_blocks_per_seq + pre_idx] : 0;
 
   const int ctx = context_lens[seq];
-  // Single-launch split-K: the sequence's partitions (at most one row of the
-  // host-sized workspace each) and the workgroups that hold some of them.
-  const int num_parts = FUSED ? min((max(ctx, 0) + kPartitionSize - 1) / kPartitionSize, max_num_partitions) : 0;
+  // Single-launch split-K: the sequence's chunks (no more than the host-sized
+  // workspace's partitions cover) and the workgroups that hold some of them.
+  const int num_parts =
+      FUSED ? min((max(ctx, 0) + chunk - 1) / chunk, max_num_partitions * (kPartitionSize / chunk)) : 0;
   const int wg_active = FUSED ? min((int)gridDim.y, (num_parts + W - 1) / W) : 0;
   if constexpr (FUSED) {
     if ((int)blockIdx.y >= wg_active) {  // no partition for this workgroup
@@ -322,8 +340,6 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     tok_end = min(ctx, tok_begin + kPartitionSize);
   }
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = wave_id();
   const int row = lane / LPT;
   const int col = lane % LPT;  // this lane's 8 dims: col*8 .. col*8+7
 
@@ -477,20 +493,22 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   // Stream blocks first, first + stride, ... (< nblk) of the range: double
   // buffered, so while a block is consumed the next one's 2*LPB loads are in
-  // flight.  The steady-state body issues unconditionally, so every consume
-  // in it waits for its own loads only; the 1-3 blocks left at the end of a
-  // window are peeled (their waits may be conservative, and no block is
-  // fetched twice).  Table entries come 64 at a time (lane k holds the entry
-  // of the wave's block j0 + k).
-  auto stream_blocks = [&](int first, int stride) {
+  // flight.  Every path into the steady-state body has issued the same two
+  // blocks' loads (a one-block window loads its block twice), so the waits the
+  // compiler places there are exact: each consume waits for its own loads
+  // only, never for the block behind it.  The 1-3 blocks left at the end of a
+  // window are peeled (their waits may be conservative).  Table entries come
+  // 64 at a time (lane k holds the entry of the wave's block j0 + k); with
+  // `pre`, the first window's are already in pre_win.
+  auto stream_blocks = [&](int first, int stride, bool pre) {
     const int nb = first < nblk ? (nblk - first + stride - 1) / stride : 0;
     uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
     for (int j0 = 0; j0 < nb; j0 += kWave) {
       const int jn = min(kWave, nb - j0);
-      const int tbl_win = lane < jn ? tbl[first + (j0 + lane) * stride] : 0;
+      const int tbl_win = pre && j0 == 0 ? pre_win : (lane < jn ? tbl[first + (j0 + lane) * stride] : 0);
       const int blk_base = first + j0 * stride;  // range-relative index of the window's block 0
       issue(uniform_lane(tbl_win, 0), ka, va);
-      if (jn > 1) issue(uniform_lane(tbl_win, 1), kb2, vb2);
+      issue(uniform_lane(tbl_win, jn > 1 ? 1 : 0), kb2, vb2);
       int j = 0;
       for (; j + 3 < jn; j += 2) {
         consume(ka, va, blk_base + j * stride, uniform_lane(tbl_win, j));
@@ -507,15 +525,16 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   };
 
   if constexpr (FUSED) {
-    // This wavefront's partitions, one running state over all of them.
+    // This wavefront's chunks, one running state over all of them.
     const int wstride = (int)gridDim.y * W;
-    for (int p = (int)blockIdx.y * W + wave; p < num_parts; p += wstride) {
-      set_range(p * kPartitionSize, min(ctx, (p + 1) * kPartitionSize));
-      stream_blocks(0, 1);
+    const int p0 = (int)blockIdx.y * W + wave;
+    for (int p = p0; p < num_parts; p += wstride) {
+      set_range(p * chunk, min(ctx, (p + 1) * chunk));
+      stream_blocks(0, 1, p == p0);
     }
   } else {
     set_range(tok_begin, tok_end);
-    stream_blocks(wave, W);
+    stream_blocks(wave, W, true);
   }
 
   // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
@@ -747,36 +766,49 @@ static hipError_t launch_decode_t(const DecodeArgs& a, int mode, hipStream_t str
     // are reversed (measured on the 64-sequence decode of the mixed step:
     // 7-11 % faster; grids of several rounds keep plain longest-first order).
     const int64_t wgs = (int64_t)a.num_seqs * a.num_kv_heads;
+    // Ordering pays only when some workgroups wait for others to finish; with
+    // no more workgroups than compute units all of them start at once.
+    const bool order = a.order_max_ctx > 0 && a.num_seqs <= kOrderMaxSeqs && (a.num_cus <= 0 || wgs > a.num_cus);
     int32_t pair_from = 0;
     if (a.num_cus > 0 && wgs > a.num_cus && wgs <= 2 * (int64_t)a.num_cus) pair_from = a.num_cus / a.num_kv_heads;
     if (pair_from >= a.num_seqs) pair_from = 0;
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kDecodeWaves, kDecodeSingle, BS>), grid,
                        dim3(kDecodeWaves * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.num_kv_heads, scale_log2, a.out, nullptr, nullptr,
-                       nullptr, 0, a.num_seqs <= kOrderMaxSeqs ? a.order_max_ctx : 0, a.new_k, a.new_v, a.k_store,
-                       a.v_store, a.num_seqs <= kOrderMaxSeqs && a.order_max_ctx > 0 ? pair_from : 0, nullptr);
+                       nullptr, 0, order ? a.order_max_ctx : 0, a.new_k, a.new_v, a.k_store,
+                       a.v_store, order ? pair_from : 0, nullptr, 0);
   } else if (mode == kDecodeSplit) {
     dim3 grid(a.num_kv_heads, a.max_num_partitions, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, kSplitWaves, kDecodeSplit, BS>), grid,
                        dim3(kSplitWaves * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.num_kv_heads, scale_log2, nullptr, a.tmp_out,
                        a.max_logits, a.exp_sums, a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store, 0,
-                       nullptr);
+                       nullptr, 0);
   } else {
     // Single launch: enough workgroups per (sequence, KV head) that every
     // wavefront of one resident round (one workgroup per compute unit) has a
-    // partition, and no more than the partitions need.
+    // chunk, and no more than the chunks need.  Chunks are 256-token
+    // partitions unless that leaves wavefronts of the round idle; then they
+    // are halved (down to 256 / FW tokens, so no more workgroups than the
+    // workspace has partition rows, and at least one block).
     constexpr int FW = fused_waves<D, G, BS>();
     const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t slots = (int64_t)(a.num_cus > 0 ? a.num_cus : 256) * (8 / FW);
-    const int64_t by_parts = (a.max_num_partitions + FW - 1) / FW;
-    const int y = (int)std::max<int64_t>(1, std::min<int64_t>(by_parts, slots / pairs));
+    const int64_t max_ctx = a.max_context_len > 0 ? std::min<int64_t>(a.max_context_len, (int64_t)a.max_num_partitions *
+                                                                                             kPartitionSize)
+                                                  : (int64_t)a.max_num_partitions * kPartitionSize;
+    int chunk = kPartitionSize;
+    while (chunk / 2 >= std::max(BS, kPartitionSize / FW) && pairs * ((max_ctx + chunk - 1) / chunk) < slots * FW)
+      chunk /= 2;
+    const int64_t by_chunks = ((max_ctx + chunk - 1) / chunk + FW - 1) / FW;
+    const int y = (int)std::max<int64_t>(
+        1, std::min<int64_t>({by_chunks, slots / pairs, (int64_t)a.max_num_partitions}));
     dim3 grid(a.num_kv_heads, y, a.num_seqs);
     hipLaunchKernelGGL((paged_decode_kernel<T, D, G, FW, kDecodeSplitFused, BS>), grid,
                        dim3(FW * kWave), 0, stream, a.q, a.k_cache, a.v_cache, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.num_kv_heads, scale_log2, a.out, a.tmp_out,
                        a.max_logits, a.exp_sums, a.max_num_partitions, 0, a.new_k, a.new_v, a.k_store, a.v_store, 0,
-                       a.counters);
+                       a.counters, chunk);
   }
   return hipGetLastError();
 }

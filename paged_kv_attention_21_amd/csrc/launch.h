@@ -43,6 +43,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t block_size;          // tokens per KV block: 8, 16 or 32
   int32_t max_num_partitions;  // split-K only
+  int32_t max_context_len;     // upper bound of context_lens (0 if unknown)
   int32_t order_max_ctx;       // single pass: > 0 runs sequences longest first (bucketed by this bound)
   int32_t num_cus;             // compute units of the device (0 if unknown)
   float scale;
