@@ -59,6 +59,15 @@ struct DecodeLayout {
   static_assert(kWave % LPT == 0 && BS % TPL == 0 && kPartitionSize % BS == 0, "unsupported head_dim / block");
 };
 
+// Wave loads per tensor in one streaming tile (see paged_decode_kernel): the
+// whole block up to four loads (two for groups of eight query heads, whose
+// accumulators and scores take twice the registers of a group of four).
+template <int D, int G, int BS>
+constexpr int decode_tile_loads() {
+  constexpr int cap = G >= 8 ? 2 : 4;
+  return DecodeLayout<D, BS>::LPB < cap ? DecodeLayout<D, BS>::LPB : cap;
+}
+
 // Heavy-first order of the single-pass grid.  Workgroups start in grid order
 // as earlier ones finish, and a long sequence that starts last sets the
 // kernel's tail, so grid row r is given the r-th sequence in decreasing
@@ -357,12 +366,23 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     app_v = *reinterpret_cast<const uint4*>(new_v + src);
   }
 
-  // q pieces of the G heads of this group.
-  uint32_t qv[G][4];
+  // q pieces of the G heads of this group: in registers, or - for groups of
+  // four and more, whose accumulators take 32+ registers per lane - in LDS,
+  // read once per tile and head.
+  constexpr bool kQLds = G >= 4;
+  __shared__ uint4 s_q[kQLds ? G : 1][kQLds ? D / 8 : 1];
+  uint32_t qv[kQLds ? 1 : G][4];
+  if constexpr (kQLds) {
+    const uint16_t* qg = q + ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;  // the group's G rows, contiguous
+    for (int t = threadIdx.x; t < G * D / 8; t += W * kWave)
+      s_q[t / (D / 8)][t % (D / 8)] = *reinterpret_cast<const uint4*>(qg + t * 8);
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 t = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + kvh * G + g) * D + col * 8);
-    qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+    for (int g = 0; g < G; ++g) {
+      const uint4 t = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + kvh * G + g) * D + col * 8);
+      qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+    }
   }
 
   float m[G], lsum[G], acc[G][8];
@@ -376,10 +396,18 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   const size_t row_elems = (size_t)num_kv_heads * D;        // elements between consecutive slots
   const size_t block_bytes = row_elems * kBlockSize * 2;    // bytes per physical block
-  // Per-lane byte offset of load i inside a (block, head): row (i*TPL + row), dims col*8.
-  uint32_t lane_off[LPB];
+  // The streaming unit is a tile: TT consecutive slots of one block, LPBT
+  // wave loads per tensor (the whole block when it needs no more than
+  // tile_loads() loads), so the load buffers and per-token scores stay within
+  // the register budget for every head size, group and block size.
+  constexpr int LPBT = decode_tile_loads<D, G, BS>();
+  constexpr int TT = LPBT * TPL;  // slots per tile
+  constexpr int TPB = LPB / LPBT;  // tiles per block
+  const uint32_t tile_bytes = (uint32_t)(row_elems * TT * 2);
+  // Per-lane byte offset of load i inside a tile: slot (i*TPL + row), dims col*8.
+  uint32_t lane_off[LPBT];
 #pragma unroll
-  for (int i = 0; i < LPB; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
+  for (int i = 0; i < LPBT; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
   const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
   const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
 
@@ -396,43 +424,64 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
   };
 
-  auto issue = [&](int pb, uint4 (&kk)[LPB], uint4 (&vv)[LPB]) {
-    const char* kb = kbase + (size_t)pb * block_bytes;
-    const char* vb = vbase + (size_t)pb * block_bytes;
+  // Loads of tile `sub` of physical block pb.
+  auto issue = [&](int pb, int sub, uint4 (&kk)[LPBT], uint4 (&vv)[LPBT]) {
+    const size_t off = (size_t)pb * block_bytes + (size_t)sub * tile_bytes;
+    const char* kb = kbase + off;
+    const char* vb = vbase + off;
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kk[i] = load_nt16(kb + lane_off[i]);
+    for (int i = 0; i < LPBT; ++i) kk[i] = load_nt16(kb + lane_off[i]);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vv[i] = load_nt16(vb + lane_off[i]);
+    for (int i = 0; i < LPBT; ++i) vv[i] = load_nt16(vb + lane_off[i]);
   };
 
-  // MASKED is only taken for the range's last block when it is partial.
-  auto consume_t = [&](auto masked, const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int nvalid) {
+  // MASKED is only taken for tiles of the range's last block that hold slots
+  // past its last token (nvalid < TT; nvalid <= 0 masks the whole tile).
+  auto consume_t = [&](auto masked, const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int nvalid) {
     constexpr bool MASKED = decltype(masked)::value;
-    float s[G][LPB];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      const bool valid = !MASKED || (i * TPL + row) < nvalid;
+    float s[G][LPBT];
+    if constexpr (kQLds) {
+      // Head by head, so only one head's q is live.
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float d = E::dot2(qv[g][0], kk[i].x, 0.f);
-        d = E::dot2(qv[g][1], kk[i].y, d);
-        d = E::dot2(qv[g][2], kk[i].z, d);
-        d = E::dot2(qv[g][3], kk[i].w, d);
-        d = group_sum<LPT>(d) * scale_log2;
-        s[g][i] = valid ? d : -INFINITY;
+        const uint4 qq = s_q[g][col];
+#pragma unroll
+        for (int i = 0; i < LPBT; ++i) {
+          const bool valid = !MASKED || (i * TPL + row) < nvalid;
+          float d = E::dot2(qq.x, kk[i].x, 0.f);
+          d = E::dot2(qq.y, kk[i].y, d);
+          d = E::dot2(qq.z, kk[i].z, d);
+          d = E::dot2(qq.w, kk[i].w, d);
+          d = group_sum<LPT>(d) * scale_log2;
+          s[g][i] = valid ? d : -INFINITY;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPBT; ++i) {
+        const bool valid = !MASKED || (i * TPL + row) < nvalid;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = E::dot2(qv[g][0], kk[i].x, 0.f);
+          d = E::dot2(qv[g][1], kk[i].y, d);
+          d = E::dot2(qv[g][2], kk[i].z, d);
+          d = E::dot2(qv[g][3], kk[i].w, d);
+          d = group_sum<LPT>(d) * scale_log2;
+          s[g][i] = valid ? d : -INFINITY;
+        }
       }
     }
-    float p[G][LPB];
+    float p[G][LPBT];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = m[g];
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) mx = fmaxf(mx, s[g][i]);
+      for (int i = 0; i < LPBT; ++i) mx = fmaxf(mx, s[g][i]);
       const float alpha = fast_exp2(m[g] - mx);
       m[g] = mx;
       float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
+      for (int i = 0; i < LPBT; ++i) {
         p[g][i] = fast_exp2(s[g][i] - mx);
         ps += p[g][i];
       }
@@ -441,7 +490,7 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
     }
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) {
+    for (int i = 0; i < LPBT; ++i) {
       const bool valid = !MASKED || (i * TPL + row) < nvalid;
       const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
       float vf[8];
@@ -461,66 +510,73 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   };
 
-  // pb: the block's physical id (used only for the appended token's store).
-  auto consume = [&](const uint4 (&kk)[LPB], const uint4 (&vv)[LPB], int blk, int pb) {
-    if (blk == nblk - 1 && append) {
-      // The range's last block holds the appended token at row last_valid - 1:
-      // load i = (last_valid - 1) / TPL, lane row (last_valid - 1) % TPL.
-      uint4 ka2[LPB], va2[LPB];
+  // Tile `sub` of the range's block blk (physical id pb, used only for the
+  // appended token's store).
+  auto consume = [&](const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int blk, int sub, int pb) {
+    const bool last = blk == nblk - 1;
+    const int nvalid = last ? last_valid - sub * TT : TT;
+    const int r = last_valid - 1 - sub * TT;  // the appended slot's row in this tile, if in [0, TT)
+    if (last && append && r >= 0 && r < TT) {
+      // Load i = r / TPL, lane row r % TPL holds the appended token.
+      uint4 ka2[LPBT], va2[LPBT];
 #pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        const bool mine = i * TPL + row == last_valid - 1;
+      for (int i = 0; i < LPBT; ++i) {
+        const bool mine = i * TPL + row == r;
         ka2[i] = mine ? app_k : kk[i];
         va2[i] = mine ? app_v : vv[i];
       }
-      if (row == (last_valid - 1) % TPL) {
-        const uint32_t off = lane_off[0] + (uint32_t)(((last_valid - 1) / TPL) * TPL * row_elems * 2);
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
-                                  off) = app_k;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + (size_t)kvh * D * 2 + (size_t)pb * block_bytes +
-                                  off) = app_v;
+      if (row == r % TPL) {
+        const size_t off = (size_t)kvh * D * 2 + (size_t)pb * block_bytes + (size_t)sub * tile_bytes + lane_off[0] +
+                           (size_t)((r / TPL) * TPL) * row_elems * 2;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + off) = app_k;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + off) = app_v;
       }
-      if (last_valid < kBlockSize)
-        consume_t(std::true_type{}, ka2, va2, last_valid);
+      if (nvalid < TT)
+        consume_t(std::true_type{}, ka2, va2, nvalid);
       else
-        consume_t(std::false_type{}, ka2, va2, kBlockSize);
-    } else if (blk == nblk - 1 && last_valid < kBlockSize) {
-      consume_t(std::true_type{}, kk, vv, last_valid);
+        consume_t(std::false_type{}, ka2, va2, TT);
+    } else if (nvalid < TT) {
+      consume_t(std::true_type{}, kk, vv, nvalid);
     } else {
-      consume_t(std::false_type{}, kk, vv, kBlockSize);
+      consume_t(std::false_type{}, kk, vv, TT);
     }
   };
 
-  // Stream blocks first, first + stride, ... (< nblk) of the range: double
-  // buffered, so while a block is consumed the next one's 2*LPB loads are in
-  // flight.  Every path into the steady-state body has issued the same two
-  // blocks' loads (a one-block window loads its block twice), so the waits the
-  // compiler places there are exact: each consume waits for its own loads
-  // only, never for the block behind it.  The 1-3 blocks left at the end of a
-  // window are peeled (their waits may be conservative).  Table entries come
-  // 64 at a time (lane k holds the entry of the wave's block j0 + k); with
-  // `pre`, the first window's are already in pre_win.
+  // Stream the tiles of blocks first, first + stride, ... (< nblk) of the
+  // range: double buffered, so while a tile is consumed the next one's
+  // 2*LPBT loads are in flight.  Every path into the steady-state body has
+  // issued the same two tiles' loads (a one-tile window loads its tile
+  // twice), so the waits the compiler places there are exact: each consume
+  // waits for its own loads only, never for the tile behind it.  The 1-3
+  // tiles left at the end of a window are peeled (their waits may be
+  // conservative).  Table entries come 64 at a time (lane k holds the entry
+  // of the wave's block j0 + k); with `pre`, the first window's are already
+  // in pre_win.  Tile u of a window is tile u % TPB of its block u / TPB.
   auto stream_blocks = [&](int first, int stride, bool pre) {
     const int nb = first < nblk ? (nblk - first + stride - 1) / stride : 0;
-    uint4 ka[LPB], va[LPB], kb2[LPB], vb2[LPB];
+    uint4 ka[LPBT], va[LPBT], kb2[LPBT], vb2[LPBT];
     for (int j0 = 0; j0 < nb; j0 += kWave) {
       const int jn = min(kWave, nb - j0);
       const int tbl_win = pre && j0 == 0 ? pre_win : (lane < jn ? tbl[first + (j0 + lane) * stride] : 0);
       const int blk_base = first + j0 * stride;  // range-relative index of the window's block 0
-      issue(uniform_lane(tbl_win, 0), ka, va);
-      issue(uniform_lane(tbl_win, jn > 1 ? 1 : 0), kb2, vb2);
-      int j = 0;
-      for (; j + 3 < jn; j += 2) {
-        consume(ka, va, blk_base + j * stride, uniform_lane(tbl_win, j));
-        issue(uniform_lane(tbl_win, j + 2), ka, va);
-        consume(kb2, vb2, blk_base + (j + 1) * stride, uniform_lane(tbl_win, j + 1));
-        issue(uniform_lane(tbl_win, j + 3), kb2, vb2);
+      const int nt = jn * TPB;
+      auto pb_of = [&](int u) { return uniform_lane(tbl_win, u / TPB); };
+      auto blk_of = [&](int u) { return blk_base + (u / TPB) * stride; };
+      issue(pb_of(0), 0, ka, va);
+      const int u1 = nt > 1 ? 1 : 0;
+      issue(pb_of(u1), u1 % TPB, kb2, vb2);
+      int u = 0;
+      for (; u + 3 < nt; u += 2) {
+        consume(ka, va, blk_of(u), u % TPB, pb_of(u));
+        issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
+        consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
+        issue(pb_of(u + 3), (u + 3) % TPB, kb2, vb2);
       }
-      const int rem = jn - j;  // 1, 2 or 3 blocks left; ka holds j, kb2 holds j + 1
-      consume(ka, va, blk_base + j * stride, uniform_lane(tbl_win, j));
-      if (rem == 3) issue(uniform_lane(tbl_win, j + 2), ka, va);
-      if (rem >= 2) consume(kb2, vb2, blk_base + (j + 1) * stride, uniform_lane(tbl_win, j + 1));
-      if (rem == 3) consume(ka, va, blk_base + (j + 2) * stride, uniform_lane(tbl_win, j + 2));
+      const int rem = nt - u;  // 1, 2 or 3 tiles left; ka holds u, kb2 holds u + 1
+      consume(ka, va, blk_of(u), u % TPB, pb_of(u));
+      if (rem == 3) issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
+      if (rem >= 2) consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
+      if (rem == 3) consume(ka, va, blk_of(u + 2), (u + 2) % TPB, pb_of(u + 2));
     }
   };
 
@@ -749,7 +805,7 @@ constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partit
 // may use the accumulation registers as well.
 template <int D, int G, int BS>
 constexpr int fused_waves() {
-  return 16 * DecodeLayout<D, BS>::LPB + 12 * G <= 100 ? 8 : 4;
+  return 16 * decode_tile_loads<D, G, BS>() + 12 * G <= 100 ? 8 : 4;
 }
 // Heavy-first ordering scans all context lengths in every workgroup; above
 // this many sequences the grid order is kept.

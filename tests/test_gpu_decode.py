@@ -218,6 +218,12 @@ GENERAL = [
     (torch.bfloat16, 8, 8, 256, 16),
     (torch.bfloat16, 16, 2, 256, 8),
     (torch.float16, 4, 1, 256, 32),
+    # groups of eight (q in LDS, two-load tiles) and 32-slot blocks of head
+    # size 256 (four tiles per block)
+    (torch.bfloat16, 16, 2, 128, 16),
+    (torch.bfloat16, 32, 4, 128, 32),
+    (torch.float16, 16, 2, 256, 32),
+    (torch.bfloat16, 8, 4, 256, 32),
 ]
 
 

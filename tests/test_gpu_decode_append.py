@@ -59,6 +59,11 @@ SHAPES = [
     (torch.float16, 8, 2, 64, 8),
     (torch.bfloat16, 8, 8, 256, 16),
     (torch.float16, 4, 1, 256, 32),
+    # groups of eight and 32-slot blocks of head size 256: blocks streamed
+    # as several tiles, the appended token in any of them
+    (torch.bfloat16, 16, 2, 128, 16),
+    (torch.float16, 16, 2, 256, 32),
+    (torch.bfloat16, 8, 4, 256, 32),
 ]
 IDS = [f"{str(s[0])[6:]}-{s[1]}q{s[2]}kv-d{s[3]}-b{s[4]}" for s in SHAPES]
 
