@@ -16,7 +16,10 @@ its average launch time, from HIP events on the launch stream) against the
 Other workloads (--workload): `splitk` (4 x 16,384-token split-K decode),
 `mixed` (KV write + decode + ragged causal prefill in one step),
 `sweep` (single-request fp16 decode at 128 / 1,024 / 4,096 tokens, next to a
-materialise-then-attend arm), `single` (the 128-token request alone).
+materialise-then-attend arm), `single` (the 128-token request alone),
+`prefill_long` (4 x 2,048 causal rows after 6,144 cached tokens), `shapes`
+(the decode batch at other head / group / block shapes), `rope_kv_write`,
+`block_manager`, `copy` (a device copy, for counter calibration).
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  Pools are rotated over several device copies so no step reads what
@@ -80,7 +83,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_step",
                    choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write",
-                            "block_manager", "prefill_long"])
+                            "block_manager", "prefill_long", "shapes"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--settle-ms", type=float, default=500.0,
                    help="untimed stepping before the first timed block (clock/power ramp), once per process")
@@ -826,6 +829,76 @@ def bench_sweep(args, pka, contexts=(128, 1024, 4096), name="sweep"):
     return res, step, False
 
 
+# Head and block shapes beyond the measured configs, each the decode step of
+# config 3's batch (contexts uniform in [100, 2048]) with that shape:
+# (label, dtype, q heads, KV heads, head size, block size).
+DECODE_SHAPES = [
+    ("G8 d128 b16 (64q/8kv)", torch.bfloat16, 64, 8, 128, 16),
+    ("G4 d128 b16 (32q/8kv)", torch.bfloat16, 32, 8, 128, 16),
+    ("G1 d128 b16 (32q/32kv, fp16)", torch.float16, 32, 32, 128, 16),
+    ("G2 d128 b32 (16q/8kv)", torch.bfloat16, 16, 8, 128, 32),
+    ("G2 d256 b32 (16q/8kv)", torch.bfloat16, 16, 8, 256, 32),
+    ("G8 d256 b32 (32q/4kv)", torch.bfloat16, 32, 4, 256, 32),
+    ("G8 d64 b16 (64q/8kv, fp16)", torch.float16, 64, 8, 64, 16),
+]
+
+
+def bench_shapes(args, pka):
+    """The dispatched decode (single pass at this batch) on each of
+    DECODE_SHAPES: us per call (events around each call, pools rotated) and
+    achieved GB/s of the algorithmic bytes."""
+    rows = {}
+    first = None
+    for label, dtype, hq, hkv, d, bs in DECODE_SHAPES:
+        rng = np.random.default_rng(args.seed)
+        n = 256 if hkv * d <= 1024 else 128
+        ctx = [int(x) for x in rng.integers(100, 2049, size=n)]
+        step = W.make_decode_step(context_lens=ctx, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                  block_size=bs, seed=args.seed)
+        P = Pools(step, args.rotate)
+        S, Hq, D = step.decode_q.shape
+        max_ctx = int(step.decode_context_lens.max())
+        ws = pka.splitk_workspace(S, Hq, D, max_ctx, "cuda:0")
+        decs = [pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx, out=P.out, workspace=ws,
+                                      prepare=True) for r in range(P.R)]
+
+        def launch(i, ev):
+            if ev:
+                ev[0].record()
+            decs[i % P.R]()
+            if ev:
+                ev[1].record()
+
+        st = {}
+        _, (dec_ms,) = timed_loop(launch, 1, args.steps, args.warmup, stats=st)
+        gbs = W.decode_bytes(step) / (dec_ms * 1e-3) / 1e9
+        rows[label] = {"num_seqs": n, "context_tokens": int(sum(ctx)), "us_per_call": round(dec_ms * 1e3, 2),
+                       "us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][0]],
+                       "algorithmic_bytes": W.decode_bytes(step), "achieved_GBps": round(gbs, 1),
+                       "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                       "variant": "single-pass" if pka.decode_choose_variant(S, hkv, max_ctx) == 1 else "split-K"}
+        log(f"{label}: {rows[label]['us_per_call']} us, {rows[label]['achieved_GBps']} GB/s")
+        if first is None:
+            first = (label, dec_ms, gbs)
+        del P, decs, ws
+        torch.cuda.empty_cache()
+    label, dec_ms, gbs = first
+    res = {
+        "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "ms_per_step": round(dec_ms, 5),
+        "per_shape": rows,
+        "dtype": "bf16",
+        "config": {"workload": "decode of 256 (128 for the largest rows) sequences with contexts uniform in "
+                               "[100, 2048], per head/block shape; value: " + label, "seed": args.seed},
+        "roofline": {"kernel": f"paged_decode_kernel ({label})", "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    return res, None, False
+
+
 def cpu_baseline_rope(step, budget_s, rows=256):
     """Time the oracle (as is) on the first `rows` new rows of the step."""
     import oracle
@@ -1109,6 +1182,8 @@ def main():
         res, step, write = bench_block_manager(args, pka)
     elif args.workload == "prefill_long":
         res, step, write = bench_prefill_long(args, pka)
+    elif args.workload == "shapes":
+        res, step, write = bench_shapes(args, pka)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
 
