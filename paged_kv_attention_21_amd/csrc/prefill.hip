@@ -185,7 +185,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, int n
 
 // Geometry of one query tile, shared by the attention and merge kernels.
 struct PfTile {
-  int seq, qt, qstart, qlen, cached, q0, kend, nsplit;
+  int tile, seq, qt, qstart, qlen, cached, q0, kend, nsplit;  // tile: index in canonical order
 };
 
 __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
@@ -194,6 +194,7 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
   if (!find_tile(qsl, num_seqs, bq, tile, &seq, &qt)) return false;
   // Uniform across the wavefront: keep it (and all that follows) in scalar
   // registers so the loops and branches below are scalar-controlled.
+  t->tile = tile;
   t->seq = __builtin_amdgcn_readfirstlane(seq);
   t->qt = __builtin_amdgcn_readfirstlane(qt);
   t->qstart = qsl[t->seq];
@@ -201,6 +202,182 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
   t->cached = context_lens[t->seq] - t->qlen;
   t->q0 = t->qt * bq;
   t->kend = t->cached + t->q0 + min(bq, t->qlen - t->q0);  // keys [0, kend) are visible to some row
+  t->nsplit = (t->kend + split_keys - 1) / split_keys;
+  return true;
+}
+
+// Heavy-first order of the (query tile, split) work items.  Workgroups start
+// in grid order as slots free up, and an item with many key tiles that starts
+// late sets the kernel's tail: in canonical order (tiles chunk by chunk) the
+// last tiles of a chunk see the most keys, so on 4 chunks of 2,048 rows after
+// 6,144 cached tokens they started last and ended ~60 us after the rest.  So
+// grid row r takes the r-th item in decreasing order of its key tiles -
+// kPfOrderBuckets buckets of that count over [1, split_keys / 64], equal
+// buckets in canonical order (longest-processing-time-first list scheduling)
+// - and the heaviest items of a mixed batch each start on their own compute
+// unit.  Every workgroup derives the same order from query_start_loc and
+// context_lens, in LDS scratch that the key tiles later overwrite.
+constexpr int kPfOrderBuckets = kWave;
+constexpr int kPfOrderMaxSeqs = 128;    // chunks the ordering handles; above, grid order is kept
+constexpr int kPfOrderMaxTiles = 8192;  // query tiles likewise
+
+// Key tiles of split s of a query tile whose keys are [0, kend).
+__device__ __forceinline__ int pf_item_tiles(int kend, int s, int split_keys) {
+  const int lo = s * split_keys;
+  const int hi = min(kend, lo + split_keys);
+  return hi > lo ? (hi - lo + kPfKeys - 1) / kPfKeys : 0;
+}
+
+// Finds the item of rank `rank` and fills *t (as pf_tile) and *split; false
+// when the batch has fewer items.  scratch: (4 kPfOrderMaxSeqs + 1 +
+// kPfOrderBuckets + NT) ints of LDS; res: 7 ints of LDS apart from it.
+template <int NT>
+__device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
+                             int num_seqs, int bq, int split_keys, int rank, int* scratch, int* res, PfTile* t,
+                             int* split) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  int* tile_start = scratch;                        // [kPfOrderMaxSeqs + 1]
+  int* cached = tile_start + kPfOrderMaxSeqs + 1;  // [kPfOrderMaxSeqs]
+  int* qlen = cached + kPfOrderMaxSeqs;
+  int* qstart = qlen + kPfOrderMaxSeqs;
+  int* hist = qstart + kPfOrderMaxSeqs;             // [kPfOrderBuckets]
+  int* part = hist + kPfOrderBuckets;               // [NT]
+  // Chunk geometry and each chunk's first tile (first wavefront).
+  if (tid < kWave) {
+    int before = 0;
+    for (int base = 0; base < num_seqs; base += kWave) {
+      const int c = base + lane;
+      int n = 0;
+      if (c < num_seqs) {
+        const int q0 = qsl[c];
+        const int ql = qsl[c + 1] - q0;
+        qstart[c] = q0;
+        qlen[c] = ql;
+        cached[c] = context_lens[c] - ql;
+        n = (ql + bq - 1) / bq;
+      }
+      int incl = n;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      if (c < num_seqs) tile_start[c] = before + incl - n;
+      before += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) tile_start[num_seqs] = before;
+  }
+  if (tid < kPfOrderBuckets) hist[tid] = 0;
+  __syncthreads();
+  const int total_tiles = tile_start[num_seqs];
+  const int max_w = (split_keys + kPfKeys - 1) / kPfKeys;
+  auto bucket = [&](int w) {  // 0 holds the heaviest items
+    return (int)((long long)(max_w - min(w, max_w)) * kPfOrderBuckets / max_w);
+  };
+  auto chunk_of = [&](int T) {  // last chunk whose first tile is <= T (chunks without tiles are skipped over)
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_start[mid] <= T) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto kend_of = [&](int c, int T) {
+    const int q0 = (T - tile_start[c]) * bq;
+    return cached[c] + q0 + min(bq, qlen[c] - q0);
+  };
+  for (int T = tid; T < total_tiles; T += NT) {
+    const int c = chunk_of(T);
+    const int kend = kend_of(c, T);
+    const int ns = (kend + split_keys - 1) / split_keys;
+    for (int s = 0; s < ns; ++s) atomicAdd(&hist[bucket(pf_item_tiles(kend, s, split_keys))], 1);
+  }
+  __syncthreads();
+  // The bucket holding position `rank` (first wavefront); res[0] = bucket or
+  // -1 past the last item, res[1] = position inside the bucket.
+  if (tid < kWave) {
+    const int cnt = hist[lane];
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    const unsigned long long hit = __ballot(cnt > 0 && incl - cnt <= rank && rank < incl);
+    if (lane == 0) res[0] = -1;
+    if (hit) {
+      const int k = __ffsll((long long)hit) - 1;
+      if (lane == k) {
+        res[0] = k;
+        res[1] = rank - (incl - cnt);
+      }
+    }
+  }
+  __syncthreads();
+  const int k = res[0];
+  if (k < 0) return false;
+  const int target = res[1];
+  // Items of bucket k in canonical order: each thread counts those of its
+  // contiguous run of tiles, a scan over the threads finds the run holding
+  // the target, and its thread walks the run.
+  const int per = (total_tiles + NT - 1) / NT;
+  const int T0 = min(total_tiles, tid * per), T1 = min(total_tiles, T0 + per);
+  int cnt = 0;
+  for (int T = T0; T < T1; ++T) {
+    const int c = chunk_of(T);
+    const int kend = kend_of(c, T);
+    const int ns = (kend + split_keys - 1) / split_keys;
+    for (int s = 0; s < ns; ++s) cnt += bucket(pf_item_tiles(kend, s, split_keys)) == k;
+  }
+  part[tid] = cnt;
+  __syncthreads();
+  if (tid < kWave) {
+    // Exclusive scan over the NT runs, 64 at a time.
+    int before = 0;
+    for (int base = 0; base < NT; base += kWave) {
+      const int v0 = part[base + lane];
+      int incl = v0;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      part[base + lane] = before + incl - v0;
+      before += __shfl(incl, kWave - 1);
+    }
+  }
+  __syncthreads();
+  if (cnt > 0 && part[tid] <= target && target < part[tid] + cnt) {
+    int left = target - part[tid];
+    for (int T = T0; T < T1; ++T) {
+      const int c = chunk_of(T);
+      const int kend = kend_of(c, T);
+      const int ns = (kend + split_keys - 1) / split_keys;
+      for (int s = 0; s < ns; ++s) {
+        if (bucket(pf_item_tiles(kend, s, split_keys)) != k) continue;
+        if (left-- == 0) {
+          res[0] = c;
+          res[1] = T - tile_start[c];
+          res[2] = s;
+          res[3] = qstart[c];
+          res[4] = qlen[c];
+          res[5] = cached[c];
+          res[6] = T;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  t->tile = __builtin_amdgcn_readfirstlane(res[6]);
+  t->seq = __builtin_amdgcn_readfirstlane(res[0]);
+  t->qt = __builtin_amdgcn_readfirstlane(res[1]);
+  *split = __builtin_amdgcn_readfirstlane(res[2]);
+  t->qstart = __builtin_amdgcn_readfirstlane(res[3]);
+  t->qlen = __builtin_amdgcn_readfirstlane(res[4]);
+  t->cached = __builtin_amdgcn_readfirstlane(res[5]);
+  t->q0 = t->qt * bq;
+  t->kend = t->cached + t->q0 + min(bq, t->qlen - t->q0);
   t->nsplit = (t->kend + split_keys - 1) / split_keys;
   return true;
 }
@@ -227,11 +404,24 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int KH = kPfKeys / 32;    // 32-key halves of a key tile
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
+  static_assert((4 * kPfOrderMaxSeqs + 1 + kPfOrderBuckets + THREADS) * 4 <= sizeof(lds), "ordering scratch");
 
   const int kvh = blockIdx.x;
-  const int split = blockIdx.z;
+  // Grid row blockIdx.y is an item rank: heavy-first when the batch is small
+  // enough for the ordering, else tile blockIdx.y / max_splits, split
+  // blockIdx.y % max_splits.  (The host sizes the grid for the upper bound.)
+  __shared__ int pick_res[7];
   PfTile tl;
-  if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, split_keys, blockIdx.y, &tl)) return;
+  int split;
+  if (num_seqs <= kPfOrderMaxSeqs && (int)gridDim.y / max(max_splits, 1) <= kPfOrderMaxTiles) {
+    if (!pf_pick_item<THREADS>(query_start_loc, context_lens, num_seqs, BQ, split_keys, (int)blockIdx.y,
+                               reinterpret_cast<int*>(lds), pick_res, &tl, &split))
+      return;
+  } else {
+    split = (int)blockIdx.y % max_splits;
+    if (!pf_tile(query_start_loc, context_lens, num_seqs, BQ, split_keys, (int)blockIdx.y / max_splits, &tl)) return;
+  }
+  const int tile_id = tl.tile;
   if (split >= tl.nsplit) return;  // this tile sees fewer keys
   if (tl.nsplit > max_splits) return;  // context longer than max_context_len: precondition broken
 
@@ -517,7 +707,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int n = wave * RPW + nt * 16 + l16;
     if (tl.nsplit > 1) {
       // Unnormalised state of this split for the merge (invalid rows too: they are never stored).
-      float* slot = partial + (((size_t)blockIdx.y * max_splits + split) * num_kv_heads + kvh) * pf_slot_floats(D);
+      float* slot = partial + (((size_t)tile_id * max_splits + split) * num_kv_heads + kvh) * pf_slot_floats(D);
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt)
         *reinterpret_cast<floatx4_t*>(slot + (size_t)n * D + 16 * dt + 4 * blk) = o[nt][dt];
@@ -666,7 +856,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   if (a.split_keys <= 0 || a.split_keys % kPfKeys) return hipErrorInvalidValue;
   const int splits = (a.max_context_len + a.split_keys - 1) / a.split_keys;
   if (tiles > 65535 || splits > 65535) return hipErrorInvalidValue;
-  dim3 grid(a.num_kv_heads, (unsigned)tiles, (unsigned)splits);
+  // One grid row per (query tile, split) item slot; rows past the batch's
+  // items exit at once.
+  if (tiles * (size_t)splits > 65535) return hipErrorInvalidValue;
+  dim3 grid(a.num_kv_heads, (unsigned)(tiles * splits));
   hipLaunchKernelGGL((paged_prefill_kernel<T, D, G, BS>), grid, dim3(PfGeom<D>::THREADS), 0, stream, a.q, a.k_cache, a.v_cache,
                      a.block_tables, a.context_lens, a.query_start_loc, a.num_seqs, a.max_blocks_per_seq,
                      a.num_kv_heads, a.split_keys, splits, a.scale * kLog2e, a.out, a.workspace);
