@@ -218,43 +218,52 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
 // unit.  Every workgroup derives the same order from query_start_loc and
 // context_lens, in LDS scratch that the key tiles later overwrite.
 constexpr int kPfOrderBuckets = kWave;
-constexpr int kPfOrderMaxSeqs = 128;    // chunks the ordering handles; above, grid order is kept
-constexpr int kPfOrderMaxTiles = 8192;  // query tiles likewise
-
-// Key tiles of split s of a query tile whose keys are [0, kend).
-__device__ __forceinline__ int pf_item_tiles(int kend, int s, int split_keys) {
-  const int lo = s * split_keys;
-  const int hi = min(kend, lo + split_keys);
-  return hi > lo ? (hi - lo + kPfKeys - 1) / kPfKeys : 0;
-}
+constexpr int kPfOrderMaxSeqs = 256;    // chunks the ordering handles; above, grid order is kept
+constexpr int kPfOrderMaxTiles = 4096;  // query tiles likewise
 
 // Finds the item of rank `rank` and fills *t (as pf_tile) and *split; false
-// when the batch has fewer items.  scratch: (4 kPfOrderMaxSeqs + 1 +
-// kPfOrderBuckets + NT) ints of LDS; res: 7 ints of LDS apart from it.
+// when the batch has fewer items.  scratch: LDS for (4 kPfOrderMaxSeqs + 1 +
+// 2 kPfOrderMaxTiles + kPfOrderBuckets + NT) ints; res: 8 ints of LDS apart
+// from it.
+//
+// Every item is a full split (split_keys / 64 key tiles, bucket 0) except the
+// last split of each query tile, which holds the tile's remaining keys.  The
+// first wavefront lays out, per query tile, its split count and the key
+// tiles of its last split (walking each chunk's tiles with running sums, no
+// divisions); the workgroup builds the bucket histogram from that, the first
+// wavefront finds the bucket holding `rank`, and a scan over per-thread runs
+// of tiles finds the tile holding the item.
 template <int NT>
 __device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
                              int num_seqs, int bq, int split_keys, int rank, int* scratch, int* res, PfTile* t,
                              int* split) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  int* tile_start = scratch;                        // [kPfOrderMaxSeqs + 1]
-  int* cached = tile_start + kPfOrderMaxSeqs + 1;  // [kPfOrderMaxSeqs]
+  int* cached = scratch;                          // [kPfOrderMaxSeqs]
   int* qlen = cached + kPfOrderMaxSeqs;
   int* qstart = qlen + kPfOrderMaxSeqs;
-  int* hist = qstart + kPfOrderMaxSeqs;             // [kPfOrderBuckets]
-  int* part = hist + kPfOrderBuckets;               // [NT]
-  // Chunk geometry and each chunk's first tile (first wavefront).
+  int* tile_start = qstart + kPfOrderMaxSeqs;     // [kPfOrderMaxSeqs + 1]
+  int* tile_geo = tile_start + kPfOrderMaxSeqs + 1;  // [kPfOrderMaxTiles]: split count << 16 | last split's key tiles
+  int* tile_chunk = tile_geo + kPfOrderMaxTiles;  // [kPfOrderMaxTiles]
+  int* hist = tile_chunk + kPfOrderMaxTiles;      // [kPfOrderBuckets]
+  int* part = hist + kPfOrderBuckets;             // [NT]
+  const int max_w = (split_keys + kPfKeys - 1) / kPfKeys;
+  // Buckets of width 2^sh over max_w - w, so that every weight lands in one.
+  const int sh = max_w > kPfOrderBuckets ? 32 - __builtin_clz((unsigned)(max_w - 1)) - 6 : 0;
+  auto bucket = [&](int w) { return min(kPfOrderBuckets - 1, (max_w - w) >> sh); };
+  if (tid < kPfOrderBuckets) hist[tid] = 0;
   if (tid < kWave) {
     int before = 0;
     for (int base = 0; base < num_seqs; base += kWave) {
       const int c = base + lane;
-      int n = 0;
+      int n = 0, ql = 0, cach = 0;
       if (c < num_seqs) {
         const int q0 = qsl[c];
-        const int ql = qsl[c + 1] - q0;
+        ql = qsl[c + 1] - q0;
+        cach = context_lens[c] - ql;
         qstart[c] = q0;
         qlen[c] = ql;
-        cached[c] = context_lens[c] - ql;
+        cached[c] = cach;
         n = (ql + bq - 1) / bq;
       }
       int incl = n;
@@ -263,35 +272,38 @@ __device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __r
         const int v = __shfl_up(incl, off);
         if (lane >= off) incl += v;
       }
-      if (c < num_seqs) tile_start[c] = before + incl - n;
+      const int first = before + incl - n;
       before += __shfl(incl, kWave - 1);
+      if (c < num_seqs) {
+        tile_start[c] = first;
+        if (before <= kPfOrderMaxTiles && n > 0) {
+          // Tile i's keys end at cached + min((i + 1) bq, ql); rem = keys of
+          // its last split, in (0, split_keys].
+          int kend = cach + min(bq, ql);
+          int ns = (kend + split_keys - 1) / split_keys;
+          int rem = kend - (ns - 1) * split_keys;
+          for (int i = 0; i < n; ++i) {
+            tile_geo[first + i] = (ns << 16) | ((rem + kPfKeys - 1) / kPfKeys);
+            tile_chunk[first + i] = c;
+            const int step = min((i + 2) * bq, ql) - min((i + 1) * bq, ql);
+            rem += step;
+            while (rem > split_keys) {
+              rem -= split_keys;
+              ++ns;
+            }
+          }
+        }
+      }
     }
     if (lane == 0) tile_start[num_seqs] = before;
   }
-  if (tid < kPfOrderBuckets) hist[tid] = 0;
   __syncthreads();
   const int total_tiles = tile_start[num_seqs];
-  const int max_w = (split_keys + kPfKeys - 1) / kPfKeys;
-  auto bucket = [&](int w) {  // 0 holds the heaviest items
-    return (int)((long long)(max_w - min(w, max_w)) * kPfOrderBuckets / max_w);
-  };
-  auto chunk_of = [&](int T) {  // last chunk whose first tile is <= T (chunks without tiles are skipped over)
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_start[mid] <= T) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
-  auto kend_of = [&](int c, int T) {
-    const int q0 = (T - tile_start[c]) * bq;
-    return cached[c] + q0 + min(bq, qlen[c] - q0);
-  };
+  if (total_tiles > kPfOrderMaxTiles) return false;  // (the caller checks the bound first)
   for (int T = tid; T < total_tiles; T += NT) {
-    const int c = chunk_of(T);
-    const int kend = kend_of(c, T);
-    const int ns = (kend + split_keys - 1) / split_keys;
-    for (int s = 0; s < ns; ++s) atomicAdd(&hist[bucket(pf_item_tiles(kend, s, split_keys))], 1);
+    const int g = tile_geo[T];
+    if ((g >> 16) > 1) atomicAdd(&hist[0], (g >> 16) - 1);
+    atomicAdd(&hist[bucket(g & 0xffff)], 1);
   }
   __syncthreads();
   // The bucket holding position `rank` (first wavefront); res[0] = bucket or
@@ -318,22 +330,18 @@ __device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __r
   const int k = res[0];
   if (k < 0) return false;
   const int target = res[1];
-  // Items of bucket k in canonical order: each thread counts those of its
-  // contiguous run of tiles, a scan over the threads finds the run holding
-  // the target, and its thread walks the run.
+  // Items of bucket k in canonical order (tiles in order, a tile's splits in
+  // order): per tile, its full splits when k = 0, then its last split if it
+  // falls in bucket k.  Each thread counts its run of tiles, a scan over the
+  // runs finds the one holding the target, and its thread walks the run.
+  auto n_in_k = [&](int g) { return (k == 0 ? (g >> 16) - 1 : 0) + (bucket(g & 0xffff) == k); };
   const int per = (total_tiles + NT - 1) / NT;
   const int T0 = min(total_tiles, tid * per), T1 = min(total_tiles, T0 + per);
   int cnt = 0;
-  for (int T = T0; T < T1; ++T) {
-    const int c = chunk_of(T);
-    const int kend = kend_of(c, T);
-    const int ns = (kend + split_keys - 1) / split_keys;
-    for (int s = 0; s < ns; ++s) cnt += bucket(pf_item_tiles(kend, s, split_keys)) == k;
-  }
+  for (int T = T0; T < T1; ++T) cnt += n_in_k(tile_geo[T]);
   part[tid] = cnt;
   __syncthreads();
   if (tid < kWave) {
-    // Exclusive scan over the NT runs, 64 at a time.
     int before = 0;
     for (int base = 0; base < NT; base += kWave) {
       const int v0 = part[base + lane];
@@ -351,21 +359,22 @@ __device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __r
   if (cnt > 0 && part[tid] <= target && target < part[tid] + cnt) {
     int left = target - part[tid];
     for (int T = T0; T < T1; ++T) {
-      const int c = chunk_of(T);
-      const int kend = kend_of(c, T);
-      const int ns = (kend + split_keys - 1) / split_keys;
-      for (int s = 0; s < ns; ++s) {
-        if (bucket(pf_item_tiles(kend, s, split_keys)) != k) continue;
-        if (left-- == 0) {
-          res[0] = c;
-          res[1] = T - tile_start[c];
-          res[2] = s;
-          res[3] = qstart[c];
-          res[4] = qlen[c];
-          res[5] = cached[c];
-          res[6] = T;
-        }
+      const int g = tile_geo[T];
+      const int n = n_in_k(g);
+      if (left < n) {
+        // The full splits come first (bucket 0 only), then the last split.
+        const int sp = k == 0 ? left : (g >> 16) - 1;
+        const int c = tile_chunk[T];
+        res[0] = c;
+        res[1] = T - tile_start[c];
+        res[2] = sp;
+        res[3] = qstart[c];
+        res[4] = qlen[c];
+        res[5] = cached[c];
+        res[6] = T;
+        break;
       }
+      left -= n;
     }
   }
   __syncthreads();
@@ -404,16 +413,18 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int KH = kPfKeys / 32;    // 32-key halves of a key tile
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
-  static_assert((4 * kPfOrderMaxSeqs + 1 + kPfOrderBuckets + THREADS) * 4 <= sizeof(lds), "ordering scratch");
+  static_assert((4 * kPfOrderMaxSeqs + 1 + 2 * kPfOrderMaxTiles + kPfOrderBuckets + THREADS) * 4 <= sizeof(lds),
+                "ordering scratch");
 
   const int kvh = blockIdx.x;
   // Grid row blockIdx.y is an item rank: heavy-first when the batch is small
   // enough for the ordering, else tile blockIdx.y / max_splits, split
   // blockIdx.y % max_splits.  (The host sizes the grid for the upper bound.)
-  __shared__ int pick_res[7];
+  __shared__ int pick_res[8];
   PfTile tl;
   int split;
   if (num_seqs <= kPfOrderMaxSeqs && (int)gridDim.y / max(max_splits, 1) <= kPfOrderMaxTiles) {
+    // (gridDim.y / max_splits bounds the batch's query tiles.)
     if (!pf_pick_item<THREADS>(query_start_loc, context_lens, num_seqs, BQ, split_keys, (int)blockIdx.y,
                                reinterpret_cast<int*>(lds), pick_res, &tl, &split))
       return;
