@@ -52,28 +52,35 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # HBM bytes per launch of each workload's dominant kernel, from rocprofv3
 # FETCH_SIZE (x 2.0, the factor a 1 GiB copy calibrates) + WRITE_SIZE runs
 # (profiles/traffic_fetch_write.md), valid only for the kernel source they were
-# taken on: (source file, sha256 prefix, bytes).
+# taken on: (source file, sha256 prefix, bytes).  The bench line names the
+# source of its traffic figure, or why it is null.
+TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode.hip", "de774b36d6497090", 1191574048),
-    "splitk": ("decode.hip", "de774b36d6497090", 271015168),
-    "rope_kv_write": ("rope_kv.hip", "39460877f67d3cc2", 34908832),
-    "mixed": ("prefill.hip", "26823a696a320f6b", 50132520),
-    "prefill_long": ("prefill.hip", "26823a696a320f6b", 201633088),
+    "decode_step": ("decode_impl.h", "3ffc39e23edfa458", 1190843392),
+    "splitk": ("decode_impl.h", "3ffc39e23edfa458", 269536870),
+    "mixed": ("prefill.hip", "7aee6fd036ca4352", 50198630),
+    "prefill_long": ("prefill.hip", "7aee6fd036ca4352", 319434752),
+    "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),
 }
 
 
 def recorded_traffic(workload):
-    """Traffic of the dominant kernel if its source is unchanged since the
-    counters were taken, else None."""
+    """(traffic bytes or None, a note on where the figure comes from): the
+    recorded counters if the dominant kernel's source is unchanged since they
+    were taken, else None."""
     import hashlib
 
     if workload not in RECORDED_TRAFFIC:
-        return None
+        return None, "no counter run recorded for this workload"
     fname, digest, nbytes = RECORDED_TRAFFIC[workload]
     path = os.path.join(ROOT, "paged_kv_attention_21_amd", "csrc", fname)
     with open(path, "rb") as f:
         now = hashlib.sha256(f.read()).hexdigest()[:16]
-    return nbytes if now == digest else None
+    if now != digest:
+        return None, (f"counters were taken on csrc/{fname} sha256 {digest}, the source is now {now}: "
+                      "not measured for this source")
+    return nbytes, (f"recorded, not measured in this run: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE per dispatch "
+                    f"({TRAFFIC_PROFILE}), kernel source csrc/{fname} sha256 {digest} (unchanged)")
 
 
 def parse_args():
@@ -206,6 +213,24 @@ def graph_batch_us(fn, batch, replays, warmup):
         b.synchronize()
         per.append(a.elapsed_time(b) * 1e3 / batch)
     return percentiles(per)
+
+
+KERNEL_BATCH = 20  # back-to-back calls per replay when timing a kernel for its roofline figure
+
+
+def back_to_back_us(call, R, warmup):
+    """Device time per call of call(r) (r = pool copy), from replays of one
+    HIP graph of KERNEL_BATCH back-to-back calls over the rotated pools: p10 /
+    p50 / p90 in microseconds.  The host launch path drops out, so the figure
+    is the kernels' time plus the gaps between dependent launches - what a
+    profiler's kernel trace averages."""
+    def fn():
+        for i in range(KERNEL_BATCH):
+            call(i % R)
+    return graph_batch_us(fn, KERNEL_BATCH, 10, warmup)
+
+
+ROOFLINE_TIMING = f"graph replay of {KERNEL_BATCH} back-to-back calls over the rotated pools, divided by {KERNEL_BATCH}"
 
 
 def graph_step_ms(capture_fns, steps, warmup):
@@ -354,7 +379,13 @@ def bench_decode_step(args, pka):
     dbytes = W.decode_bytes(step)
     wbytes = W.kv_write_bytes(step)
     value = (dbytes + wbytes) / (wall_ms * 1e-3) / 1e9
-    achieved = (dbytes + wbytes) / (fused_ms * 1e-3) / 1e9
+    kern_us = None
+    if not args.no_graph:
+        kern_us = back_to_back_us(lambda r: pka.paged_attn_decode_append(P.q, P.new_k, P.new_v, P.k[r], P.v[r], P.bt,
+                                                                         P.cl, step.scale, max_ctx, out=P.out,
+                                                                         workspace=ws), P.R, args.warmup)
+    kern_ms = kern_us[1] * 1e-3 if kern_us else fused_ms
+    achieved = (dbytes + wbytes) / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
         "value": round(value, 2),
@@ -364,6 +395,7 @@ def bench_decode_step(args, pka):
         "eager_ms_per_step": round(eager_ms, 4),
         "decode_us_per_call": round(fused_ms * 1e3, 2),
         "decode_us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][0]],
+        "kernel_us_back_to_back_p10_p50_p90": None if kern_us is None else [round(x, 2) for x in kern_us],
         "kv_write": "folded into the decode launch (pka_paged_attn_decode_append)",
         "separate_write_then_decode": separate,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -382,6 +414,8 @@ def bench_decode_step(args, pka):
                        else "split-K decode + reduce (KV write folded in)"),
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "timing": ROOFLINE_TIMING if kern_us else "HIP events around each call",
+            "us_per_launch": round(kern_ms * 1e3, 2),
         },
     }
     return res, step, True
@@ -445,7 +479,12 @@ def bench_splitk(args, pka):
         graph_ms = graph_step_ms([step_fn(r) for r in range(P.R)], args.steps, args.warmup)
         wall_ms = graph_ms
     value = dbytes / (wall_ms * 1e-3) / 1e9
-    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    kern_us = None
+    if not args.no_graph:
+        kern_us = back_to_back_us(lambda r: pka.paged_attn_decode(P.q, P.k[r], P.v[r], P.bt, P.cl, step.scale, max_ctx,
+                                                                   out=P.out, workspace=ws), P.R, args.warmup)
+    kern_ms = kern_us[1] * 1e-3 if kern_us else dec_ms
+    achieved = dbytes / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": "paged decode µs/call + achieved HBM GB/s (% of 8 TB/s peak), 1 MI355X",
         "value": round(value, 2),
@@ -455,6 +494,7 @@ def bench_splitk(args, pka):
         "eager_ms_per_step": round(eager_ms, 4),
         "decode_us_per_call": round(dec_ms * 1e3, 2),
         "decode_us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][0]],
+        "kernel_us_back_to_back_p10_p50_p90": None if kern_us is None else [round(x, 2) for x in kern_us],
         "two_launch_partition_then_reduce": two_launch,
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "dtype": "bf16",
@@ -469,6 +509,8 @@ def bench_splitk(args, pka):
             "kernel": "paged_decode_kernel (split-K partitions + in-kernel merge, one launch)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "timing": ROOFLINE_TIMING if kern_us else "HIP events around each call",
+            "us_per_launch": round(kern_ms * 1e3, 2),
         },
     }
     return res, step, False
@@ -564,6 +606,13 @@ def bench_mixed(args, pka):
     tflops = flops / (pre_ms * 1e-3) / 1e12
     value = (dbytes + wbytes + pbytes) / (wall_ms * 1e-3) / 1e9
     ceiling = None if args.no_arms else gemm_ceiling_tflops()
+    # The roofline's time: the prefill call (attention + split merge) back to back.
+    kern_us = None
+    if not args.no_graph:
+        kern_us = back_to_back_us(lambda r: pka.paged_attn_prefill(qp, P.k[r], P.v[r], btp, clp, P.qsl, step.scale, mql,
+                                                                   mcl, out=op, workspace=pws), P.R, args.warmup)
+    kern_ms = kern_us[1] * 1e-3 if kern_us else pre_ms
+    kern_tflops = flops / (kern_ms * 1e-3) / 1e12
 
     # Two-stream schedule of the same step (comparison arm): after the KV
     # write, the HBM-bound decode runs on a second stream beside the
@@ -607,6 +656,7 @@ def bench_mixed(args, pka):
         "decode_GBps": round(dbytes / (dec_ms * 1e-3) / 1e9, 1),
         "prefill_us_per_call": round(pre_ms * 1e3, 2),
         "prefill_TFLOPs": round(tflops, 1),
+        "prefill_us_back_to_back_p10_p50_p90": None if kern_us is None else [round(x, 2) for x in kern_us],
         "unified_arm_us_per_call": None if args.no_arms else round(uni_ms * 1e3, 2),
         "unified_vs_split_attention": None if args.no_arms else round(uni_ms / (dec_ms + pre_ms), 2),
         "two_stream_ms_per_step": None if two_ms is None else round(two_ms, 4),
@@ -622,12 +672,14 @@ def bench_mixed(args, pka):
                             "prefill_flops": flops},
         },
         "roofline": {
-            "kernel": "paged_prefill_kernel", "bound": "mfma", "achieved": round(tflops, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "kernel": "paged_prefill_kernel + paged_prefill_merge_kernel (one prefill call)", "bound": "mfma",
+            "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "timing": ROOFLINE_TIMING if kern_us else "HIP events around each call",
+            "us_per_launch": round(kern_ms * 1e3, 2),
             # What a plain library GEMM reaches on this GPU, beside the spec peak.
             "measured_ceiling": ceiling,
-            "frac_of_measured_ceiling": None if ceiling is None else round(tflops / ceiling["TFLOPs"], 4),
+            "frac_of_measured_ceiling": None if ceiling is None else round(kern_tflops / ceiling["TFLOPs"], 4),
         },
     }
     return res, step, True
@@ -694,7 +746,8 @@ def bench_prefill_long(args, pka):
         "roofline": {
             "kernel": "paged_prefill_kernel", "bound": "mfma", "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "measured_ceiling": ceiling,
+            "traffic": None, "timing": "HIP events around each call (one launch: no split to merge)",
+            "us_per_launch": round(pre_ms * 1e3, 2), "measured_ceiling": ceiling,
             "frac_of_measured_ceiling": None if ceiling is None else round(tflops / ceiling["TFLOPs"], 4),
         },
     }
@@ -1204,7 +1257,7 @@ def main():
     }
     out.update(res)
     if isinstance(out.get("roofline"), dict):
-        out["roofline"]["traffic"] = recorded_traffic(args.workload)
+        out["roofline"]["traffic"], out["roofline"]["traffic_source"] = recorded_traffic(args.workload)
     if "cpu_baseline" in out:
         pass  # the workload timed its own oracle sample
     elif not args.no_cpu_baseline and step is not None:
