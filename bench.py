@@ -406,7 +406,7 @@ def bench_decode_step(args, pka):
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": step.num_kv_heads, "head_dim": D,
             "block_size": step.block_size, "context_tokens": int(step.context_lens.sum()),
             "max_context_len": max_ctx, "pool_blocks": step.num_blocks, "pool_copies_rotated": P.R,
-            "decode_variant": "single-pass" if variant == 1 else "split-K + reduce", "seed": args.seed,
+            "decode_variant": "single-pass" if variant == 1 else "split-K (one launch)", "seed": args.seed,
             "algorithmic_bytes": {"decode": dbytes, "kv_write": wbytes},
         },
         "roofline": {
