@@ -782,39 +782,40 @@ paged_prefill_merge_kernel(const int32_t* __restrict__ context_lens, const int32
   const float* lrow = mrow + kPfRows;
   const int ns = tl.nsplit;
 
-  float mm = kNegBig;
-  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, mrow[s * slot_stride]);
-
-  float lt = 0.f;
+  // One pass over the splits, UNROLL at a time with all their loads in
+  // flight: a running maximum rescales what has been accumulated, so the
+  // maxima need no round trip of their own.
+  float mm = kNegBig, lt = 0.f;
   floatx4_t acc[F4];
 #pragma unroll
   for (int c = 0; c < F4; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + UNROLL <= ns; s += UNROLL) {
+  for (int s0 = 0; s0 < ns; s0 += UNROLL) {
     floatx4_t o[UNROLL][F4];
-    float w[UNROLL], l[UNROLL];
+    float mu[UNROLL], lu[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const float* sl = base + (size_t)(s + u) * slot_stride;
-      w[u] = mrow[(s + u) * slot_stride];
-      l[u] = lrow[(s + u) * slot_stride];
+      const int s = min(s0 + u, ns - 1);  // past the last split: reloads it, weighted 0 below
+      const float* sl = base + (size_t)s * slot_stride;
+      mu[u] = mrow[s * slot_stride];
+      lu[u] = lrow[s * slot_stride];
 #pragma unroll
       for (int c = 0; c < F4; ++c) o[u][c] = *reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + d0 + 4 * c);
     }
+    float mnew = mm;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) mnew = fmaxf(mnew, mu[u]);
+    const float sc = fast_exp2(mm - mnew);
+    lt *= sc;
+#pragma unroll
+    for (int c = 0; c < F4; ++c) acc[c] *= sc;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const float wu = fast_exp2(w[u] - mm);
-      lt += wu * l[u];
+      const float wu = s0 + u < ns ? fast_exp2(mu[u] - mnew) : 0.f;
+      lt += wu * lu[u];
 #pragma unroll
       for (int c = 0; c < F4; ++c) acc[c] += wu * o[u][c];
     }
-  }
-  for (; s < ns; ++s) {
-    const float* sl = base + (size_t)s * slot_stride;
-    const float wu = fast_exp2(mrow[s * slot_stride] - mm);
-    lt += wu * lrow[s * slot_stride];
-#pragma unroll
-    for (int c = 0; c < F4; ++c) acc[c] += wu * *reinterpret_cast<const floatx4_t*>(sl + (size_t)n * D + d0 + 4 * c);
+    mm = mnew;
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* op = out + ((size_t)(tl.qstart + pos) * num_q_heads + kvh * G + n % G) * D + d0;
