@@ -152,15 +152,20 @@ __host__ __device__ constexpr size_t pf_slot_floats(int D) { return (size_t)kPfR
 
 // Find the chunk and the query tile of global tile index `tile` (tiles of
 // `bq` positions, numbered chunk by chunk).  Every wavefront runs the same scan.
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, int num_seqs, int bq, int tile,
-                                          int* seq, int* qtile) {
+// Returns, besides the chunk and its query tile, the chunk's first row, row
+// count and cached length, read in the same pass (one load round trip).
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
+                                          int num_seqs, int bq, int tile, int* seq, int* qtile, int* qstart,
+                                          int* qlen, int* cached) {
   const int lane = threadIdx.x & (kWave - 1);
   int before = 0;  // tiles of chunks already passed
   for (int base = 0; base < num_seqs; base += kWave) {
     const int s = base + lane;
-    int n = 0;
+    int n = 0, q0 = 0, ql = 0, cl = 0;
     if (s < num_seqs) {
-      const int ql = qsl[s + 1] - qsl[s];
+      q0 = qsl[s];
+      ql = qsl[s + 1] - q0;
+      cl = context_lens[s];
       n = (ql + bq - 1) / bq;
     }
     int incl = n;  // inclusive prefix sum over the wavefront
@@ -176,6 +181,9 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ qsl, int n
       const int excl = __shfl(before + incl - n, first);
       *seq = base + first;
       *qtile = tile - excl;
+      *qstart = __shfl(q0, first);
+      *qlen = __shfl(ql, first);
+      *cached = __shfl(cl - ql, first);
       return true;
     }
     before += __shfl(incl, kWave - 1);
@@ -190,16 +198,16 @@ struct PfTile {
 
 __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
                                         int num_seqs, int bq, int split_keys, int tile, PfTile* t) {
-  int seq, qt;
-  if (!find_tile(qsl, num_seqs, bq, tile, &seq, &qt)) return false;
+  int seq, qt, qstart, qlen, cached;
+  if (!find_tile(qsl, context_lens, num_seqs, bq, tile, &seq, &qt, &qstart, &qlen, &cached)) return false;
   // Uniform across the wavefront: keep it (and all that follows) in scalar
   // registers so the loops and branches below are scalar-controlled.
   t->tile = tile;
   t->seq = __builtin_amdgcn_readfirstlane(seq);
   t->qt = __builtin_amdgcn_readfirstlane(qt);
-  t->qstart = qsl[t->seq];
-  t->qlen = qsl[t->seq + 1] - t->qstart;
-  t->cached = context_lens[t->seq] - t->qlen;
+  t->qstart = __builtin_amdgcn_readfirstlane(qstart);
+  t->qlen = __builtin_amdgcn_readfirstlane(qlen);
+  t->cached = __builtin_amdgcn_readfirstlane(cached);
   t->q0 = t->qt * bq;
   t->kend = t->cached + t->q0 + min(bq, t->qlen - t->q0);  // keys [0, kend) are visible to some row
   t->nsplit = (t->kend + split_keys - 1) / split_keys;
