@@ -58,8 +58,8 @@ TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
     "decode_step": ("decode_impl.h", "3ffc39e23edfa458", 1190843392),
     "splitk": ("decode_impl.h", "3ffc39e23edfa458", 269536870),
-    "mixed": ("prefill.hip", "7aee6fd036ca4352", 50198630),
-    "prefill_long": ("prefill.hip", "7aee6fd036ca4352", 319434752),
+    "mixed": ("prefill.hip", "f3a7a434c9bc9410", 50191565),
+    "prefill_long": ("prefill.hip", "f3a7a434c9bc9410", 319682867),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),
 }
 
