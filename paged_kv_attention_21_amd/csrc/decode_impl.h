@@ -17,7 +17,13 @@
 // The workgroup's W wavefronts take the range's KV blocks round-robin.  The
 // single pass runs the sequences longest first (see heavy_first_seq).
 //
-// Lane layout inside a wavefront.  One 16-byte load per lane (8 elements)
+// Two per-wavefront computations share that frame: the vector path below for
+// groups of one and two query heads, and for groups of four and eight - whose
+// dot products and weighted sums would bound the vector path - the
+// matrix-core path (see DecodeMfma), which streams 16-key units instead of
+// blocks.
+//
+// Lane layout inside a wavefront (vector path).  One 16-byte load per lane (8 elements)
 // makes a token row of D elements span LPT = D / 8 lanes, so one wave load
 // covers TPL = 64 / LPT tokens and a 16-token block of one head takes
 // LPB = 16 / TPL loads per tensor (D = 128: 16 lanes, 4 tokens, 4 loads);
@@ -36,7 +42,8 @@
 // with them and ~5.2 TB/s without).  Block-table entries are fetched 64 at a time with one
 // vector load per wavefront and broadcast with readlane.
 //
-// Numerics: q.k in fp32 with v_dot2 on the raw fp16/bf16 pairs; softmax in the
+// Numerics: q.k in fp32 with v_dot2 on the raw fp16/bf16 pairs (matrix-core
+// path: MFMA, fp32 accumulation of exact products); softmax in the
 // base-2 domain (scale * log2 e folded into the logit); fp32 accumulation;
 // tokens past the context are selected out (never multiplied by a zero
 // weight), so NaN garbage in unowned slots cannot leak in.
@@ -66,6 +73,114 @@ template <int D, int G, int BS>
 constexpr int decode_tile_loads() {
   constexpr int cap = G >= 8 ? 2 : 4;
   return DecodeLayout<D, BS>::LPB < cap ? DecodeLayout<D, BS>::LPB : cap;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core path (groups of four and eight query heads).
+//
+// With G query heads per K/V byte the vector path's dot products, row sums and
+// weighted sums grow with G, and at G = 8 they - not HBM - bound the kernel.
+// Groups of four and more run on the matrix cores instead, in units of 16
+// consecutive keys:
+//   S^T[16 keys][16 cols] = K[16 keys][D] . Q^T[D][16 cols]
+//     (v_mfma_f32_16x16x32, the group's G heads in the first G columns of the
+//     B operand, the other columns zero and never stored),
+//   O^T[D][16 cols] += V^T[D][16 keys] . P^T[16 keys][16 cols]
+//     (v_mfma_f32_16x16x16; the accumulator layout of S^T - lane l holds keys
+//     4 (l / 16) .. +3 of column l % 16 - is exactly the B operand layout of
+//     this product, so the weights never leave the lane).
+// The weights are split into a high part (rounded to the input type) and the
+// rounded remainder, two products per unit, so they keep about 16 bits: the
+// result carries the same single output rounding as the vector path.
+// K and V rows are loaded with whole-row 16-byte pieces per lane (the same
+// coalesced pattern as the vector path), staged in a wavefront-private LDS
+// tile, and read back as operands: K rows as 16-byte A-operand pieces, V
+// through the transposing read.  Row strides of 2D + 16 bytes (K) and 2D + 32
+// bytes (V) keep both read patterns free of bank conflicts.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct DecodeMfma;
+
+template <>
+struct DecodeMfma<BF16> {
+  typedef __bf16 x8_t __attribute__((ext_vector_type(8)));
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8_t, a), __builtin_bit_cast(x8_t, b), c, 0, 0,
+                                                   0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c, 0,
+                                                     0, 0);
+  }
+};
+
+template <>
+struct DecodeMfma<F16> {
+  typedef _Float16 x8_t __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4_t __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8_t, a), __builtin_bit_cast(x8_t, b), c, 0, 0,
+                                                  0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4_t, a), __builtin_bit_cast(x4_t, b), c, 0, 0,
+                                                 0);
+  }
+};
+
+// Growth of a column's max (base 2) tolerated before the accumulators are
+// rescaled: weights stay below 2^8, well inside the input type's range.
+constexpr float kMcSlack = 8.f;
+
+// Groups that take the matrix-core path.
+template <int G>
+constexpr bool decode_uses_mfma() {
+  return G >= 4;
+}
+
+// Wavefronts per SIMD the kernel is compiled for at least: two for the
+// matrix-core path up to 128 dims, whose ring of loads and accumulators would
+// otherwise spread over the accumulation registers and run one wavefront per
+// SIMD.  At 256 dims one unit's loads and the accumulators alone take 128
+// registers, so those instances keep one wavefront per SIMD.
+template <int D, int G>
+constexpr int decode_min_waves() {
+  return decode_uses_mfma<G>() && D <= 128 ? 2 : 1;
+}
+
+// Geometry of the matrix-core path for head size D.
+template <int D>
+struct McGeom {
+  static constexpr int NL = D / 32;            // 16-byte loads per lane, per tensor and unit (= QK k-steps)
+  static constexpr int KSTR = 2 * D + 16;      // LDS row stride of the K tile, bytes
+  static constexpr int VSTR = 2 * D + 32;      // LDS row stride of the V tile, bytes
+  static constexpr int TILE = 16 * (KSTR + VSTR);  // one wavefront's K and V tiles
+  // Units whose loads are in flight at once (registers: 8 * NL per unit).
+  static constexpr int RING = D == 64 ? 4 : 2;
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// output lane i gets element i % 4 of the 8-byte pieces read by input lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4: when input lane L reads row
+// r0 + L / 4, columns c0 + 4 (L % 4) .. +3 of a row-major [key][dim] tile,
+// output lane i holds keys r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ uint2 lds_read_tr_b16(const void* p) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  const auto r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // Heavy-first order of the single-pass grid.  Workgroups start in grid order
@@ -278,7 +393,7 @@ enum DecodeMode : int {
 // the result as one state (row y of the workspace), and the last of the
 // sequence's workgroups to arrive merges those states into the output.
 template <typename T, int D, int G, int W, int MODE, int BS>
-__global__ void __launch_bounds__(W * kWave)
+__global__ void __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G>())))
 paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                     const int32_t* __restrict__ context_lens, int32_t max_blocks_per_seq,
@@ -319,12 +434,19 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // the 256-token partition, or a power-of-two fraction of it (at least one
   // KV block) when the device would otherwise be short of wavefronts; the
   // host keeps the workgroup count within the workspace's rows.
+  // The matrix-core path streams 16-key units instead of blocks: lane k then
+  // holds the entry of the wavefront's k-th unit (and, with 8-token blocks,
+  // of the unit's second block in pre_win2).
+  constexpr bool kMfma = decode_uses_mfma<G>();
   const int chunk = FUSED ? split_chunk : kPartitionSize;
-  constexpr int kPartBlocks = kPartitionSize / BS;
-  const int pre_first = FUSED ? ((int)blockIdx.y * W + wave) * (chunk / BS)
-                              : (MODE == kDecodeSplit ? part * kPartBlocks : 0) + wave;
-  const int pre_idx = pre_first + lane * (FUSED ? 1 : W);
-  const int pre_win = pre_idx < max_blocks_per_seq ? block_tables[(size_t)seq * max_blocks_per_seq + pre_idx] : 0;
+  constexpr int kStep = kMfma ? 16 : BS;  // tokens per streaming step
+  const int pre_first = FUSED ? ((int)blockIdx.y * W + wave) * (chunk / kStep)
+                              : (MODE == kDecodeSplit ? part * (kPartitionSize / kStep) : 0) + wave;
+  const int pre_step = pre_first + lane * (FUSED ? 1 : W);
+  const int pre_idx = !kMfma ? pre_step : (BS == 8 ? 2 * pre_step : (BS == 32 ? pre_step >> 1 : pre_step));
+  const int32_t* const tbl_row = block_tables + (size_t)seq * max_blocks_per_seq;
+  const int pre_win = pre_idx < max_blocks_per_seq ? tbl_row[pre_idx] : 0;
+  const int pre_win2 = kMfma && BS == 8 && pre_idx + 1 < max_blocks_per_seq ? tbl_row[pre_idx + 1] : 0;
 
   const int ctx = context_lens[seq];
   // Single-launch split-K: the sequence's chunks (no more than the host-sized
@@ -359,273 +481,516 @@ paged_decode_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // cached copy may be stale or NaN until then: it is loaded and selected
   // out, never read back) and stores the row to its slot, whose block it
   // already holds, so no extra table lookup delays the start of the loop.
+  // (The matrix-core path loads it where it is used.)
   uint4 app_k = make_uint4(0, 0, 0, 0), app_v = app_k;
-  if (new_k != nullptr && ctx > 0 && (FUSED || tok_end == ctx)) {
+  if (!kMfma && new_k != nullptr && ctx > 0 && (FUSED || tok_end == ctx)) {
     const size_t src = ((size_t)seq * num_kv_heads + kvh) * D + col * 8;
     app_k = *reinterpret_cast<const uint4*>(new_k + src);
     app_v = *reinterpret_cast<const uint4*>(new_v + src);
   }
 
-  // q pieces of the G heads of this group: in registers, or - for groups of
-  // four and more, whose accumulators take 32+ registers per lane - in LDS,
-  // read once per tile and head.
-  constexpr bool kQLds = G >= 4;
-  __shared__ uint4 s_q[kQLds ? G : 1][kQLds ? D / 8 : 1];
-  uint32_t qv[kQLds ? 1 : G][4];
-  if constexpr (kQLds) {
-    const uint16_t* qg = q + ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;  // the group's G rows, contiguous
-    for (int t = threadIdx.x; t < G * D / 8; t += W * kWave)
-      s_q[t / (D / 8)][t % (D / 8)] = *reinterpret_cast<const uint4*>(qg + t * 8);
-    __syncthreads();
-  } else {
+  // Per-wavefront states (running max in base 2, exp-sum, accumulators),
+  // merged through LDS below.  The matrix-core path keeps its K/V tiles in
+  // s_kv and writes its states over them.
+  __shared__ float s_m[W][G], s_l[W][G];
+  __shared__ float s_acc_v[kMfma ? 1 : W][G][D];
+  __shared__ __align__(16) char s_kv[kMfma ? W * McGeom<D>::TILE : 16];
+  float(*const s_acc)[G][D] = kMfma ? reinterpret_cast<float(*)[G][D]>(s_kv) : s_acc_v;
+  if constexpr (kMfma) {
+    // Matrix-core path: the wavefront streams 16-key units (see the notes
+    // above DecodeMfma); its state is the running max m_ref (base 2, per
+    // column), the lane's share of the exp-sum and the O^T accumulators.
+    using MC = DecodeMfma<T>;
+    using MG = McGeom<D>;
+    constexpr int NL = MG::NL, RING = MG::RING, KSTR = MG::KSTR, VSTR = MG::VSTR;
+    constexpr int DT = D / 16;            // 16-dim tiles of the output
+    constexpr int RB = BS == 8 ? 8 : 16;  // rows of a unit that lie in one block
+    const int g4 = lane >> 4, c16 = lane & 15;
+    char* const s_k = s_kv + wave * MG::TILE;
+    char* const s_v = s_k + 16 * KSTR;
+    const size_t row_elems = (size_t)num_kv_heads * D;  // elements between consecutive slots
+    const size_t row_bytes = row_elems * 2;
+    const size_t block_bytes = row_bytes * BS;
+    const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
+    const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
+    // Unit row TPL * i + row is this lane's row of load i; its piece is dims
+    // col * 8 .. +7.  Load i reads a uniform base plus this one lane offset.
+    const uint32_t lane_off = (uint32_t)(((size_t)row * row_elems + (size_t)col * 8) * 2);
+
+    // Q^T as the B operand: lane l holds dims 32 s + 8 (l / 16) .. +7 of the
+    // group's head l % 16 (zero for columns past the group).
+    uint4 qt[NL];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 t = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + kvh * G + g) * D + col * 8);
-      qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+    for (int s = 0; s < NL; ++s) {
+      qt[s] = make_uint4(0, 0, 0, 0);
+      if (c16 < G)
+        qt[s] = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + (size_t)kvh * G + c16) * D + 32 * s +
+                                                8 * g4);
     }
-  }
-
-  float m[G], lsum[G], acc[G][8];
+    f32x4_t o[DT];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegBig;
-    lsum[g] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[g][d] = 0.f;
-  }
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = kNegBig, l_part = 0.f;
 
-  const size_t row_elems = (size_t)num_kv_heads * D;        // elements between consecutive slots
-  const size_t block_bytes = row_elems * kBlockSize * 2;    // bytes per physical block
-  // The streaming unit is a tile: TT consecutive slots of one block, LPBT
-  // wave loads per tensor (the whole block when it needs no more than
-  // tile_loads() loads), so the load buffers and per-token scores stay within
-  // the register budget for every head size, group and block size.
-  constexpr int LPBT = decode_tile_loads<D, G, BS>();
-  constexpr int TT = LPBT * TPL;  // slots per tile
-  constexpr int TPB = LPB / LPBT;  // tiles per block
-  const uint32_t tile_bytes = (uint32_t)(row_elems * TT * 2);
-  // Per-lane byte offset of load i inside a tile: slot (i*TPL + row), dims col*8.
-  uint32_t lane_off[LPBT];
+    // The range being streamed: units [u_first, u_first + u_count), tokens
+    // up to e_tok, its last block, and whether it ends with the appended token.
+    int u_first = 0, u_count = 0, e_tok = 0, last_blk = 0;
+    bool append = false;
+    auto set_range = [&](int b, int e) __attribute__((always_inline)) {  // b: a multiple of 16
+      u_first = b / 16;
+      u_count = e > b ? (e - b + 15) / 16 : 0;
+      e_tok = e;
+      last_blk = e > 0 ? (e - 1) / BS : 0;
+      append = new_k != nullptr && ctx > 0 && e == ctx;
+    };
+    // Uniform byte offset of load i of unit u (blocks pb0 and, for 8-token
+    // blocks, pb1); the lane adds lane_off.
+    auto load_base = [&](int i, int u, int pb0, int pb1) __attribute__((always_inline)) {
+      const size_t half = BS == 32 ? (size_t)((u & 1) * 16) * row_bytes : 0;
+      const size_t base = (BS == 8 && TPL * i >= 8) ? (size_t)pb1 * block_bytes : (size_t)pb0 * block_bytes + half;
+      return base + (size_t)((TPL * i) % RB) * row_bytes;
+    };
+    uint4 kb[RING][NL], vb[RING][NL];
+    auto issue = [&](auto rb, int u, int pb0, int pb1) __attribute__((always_inline)) {
+      constexpr int r = decltype(rb)::value;
 #pragma unroll
-  for (int i = 0; i < LPBT; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
-  const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
-
-  // The range being streamed: its blocks, the tokens in its last block, and
-  // whether it ends with the appended token.
-  int nblk = 0, last_valid = 0;
-  bool append = false;
-  const int32_t* tbl = block_tables;
-  auto set_range = [&](int b, int e) {
-    const int lb_begin = b / kBlockSize;
-    nblk = e > b ? (e - b + kBlockSize - 1) / kBlockSize : 0;
-    last_valid = e - (lb_begin + nblk - 1) * kBlockSize;
-    append = new_k != nullptr && ctx > 0 && e == ctx;
-    tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
-  };
-
-  // Loads of tile `sub` of physical block pb.
-  auto issue = [&](int pb, int sub, uint4 (&kk)[LPBT], uint4 (&vv)[LPBT]) {
-    const size_t off = (size_t)pb * block_bytes + (size_t)sub * tile_bytes;
-    const char* kb = kbase + off;
-    const char* vb = vbase + off;
+      for (int i = 0; i < NL; ++i) kb[r][i] = load_nt16(kbase + load_base(i, u, pb0, pb1) + lane_off);
 #pragma unroll
-    for (int i = 0; i < LPBT; ++i) kk[i] = load_nt16(kb + lane_off[i]);
-#pragma unroll
-    for (int i = 0; i < LPBT; ++i) vv[i] = load_nt16(vb + lane_off[i]);
-  };
+      for (int i = 0; i < NL; ++i) vb[r][i] = load_nt16(vbase + load_base(i, u, pb0, pb1) + lane_off);
+    };
 
-  // MASKED is only taken for tiles of the range's last block that hold slots
-  // past its last token (nvalid < TT; nvalid <= 0 masks the whole tile).
-  auto consume_t = [&](auto masked, const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int nvalid) {
-    constexpr bool MASKED = decltype(masked)::value;
-    float s[G][LPBT];
+    // One unit: stage it in LDS, S^T by MFMA, online softmax per column,
+    // O^T += V^T (hi + lo weights).  MASKED: the range's last unit, whose
+    // rows from nvalid on lie past the range (their V rows are zeroed and
+    // their logits selected out, so NaN garbage there cannot leak in) and
+    // which may hold the appended token.
+    auto consume_t = [&](auto masked, uint4 (&kk)[NL], uint4 (&vv)[NL], int u, int nvalid, int pb0,
+                         int pb1) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
+      if constexpr (MASKED) {
+        if (append && u == u_first + u_count - 1) {
+          // The appended token is the range's last row: take it from
+          // registers and store it to its slot (whose block this unit holds).
+          const int ra = nvalid - 1;
+          const size_t src = ((size_t)seq * num_kv_heads + kvh) * D + col * 8;
+          const uint4 ak = *reinterpret_cast<const uint4*>(new_k + src);
+          const uint4 av = *reinterpret_cast<const uint4*>(new_v + src);
+#pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            if (TPL * i + row == ra) {
+              kk[i] = ak;
+              vv[i] = av;
+              const size_t off = (size_t)kvh * D * 2 + load_base(i, u, pb0, pb1) + lane_off;
+              *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + off) = ak;
+              *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + off) = av;
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          if (TPL * i + row >= nvalid) vv[i] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int rr = TPL * i + row;
+        *reinterpret_cast<uint4*>(s_k + rr * KSTR + col * 16) = kk[i];
+        *reinterpret_cast<uint4*>(s_v + rr * VSTR + col * 16) = vv[i];
+      }
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NL; ++s)
+        sc = MC::qk(*reinterpret_cast<const uint4*>(s_k + c16 * KSTR + 64 * s + 16 * g4), qt[s], sc);
+      float t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        t[i] = sc[i] * scale_log2;
+        if constexpr (MASKED) t[i] = 4 * g4 + i < nvalid ? t[i] : -INFINITY;
+      }
+      // Column max over the unit's 16 keys (lanes l, l ^ 16, l ^ 32, l ^ 48).
+      const float mx = xor32_max(xor16_max(vmax(vmax(t[0], t[1]), vmax(t[2], t[3]))));
+      // Rescale only when some column's max grew by more than kMcSlack.
+      if (__ballot(mx > m_ref + kMcSlack)) {
+        const float mn = fmaxf(m_ref, mx);
+        const float alpha = fast_exp2(m_ref - mn);
+        m_ref = mn;
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(t[i] - m_ref);
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+      const uint32_t h01 = E::pack2(p[0], p[1]), h23 = E::pack2(p[2], p[3]);
+      const uint2 ph = make_uint2(h01, h23);
+      const uint2 pl = make_uint2(E::pack2(p[0] - E::lo(h01), p[1] - E::hi(h01)),
+                                  E::pack2(p[2] - E::lo(h23), p[3] - E::hi(h23)));
+      // V^T operand of dim tile dt: input lane j of group g4 reads row
+      // 4 g4 + j / 4, dims 16 dt + 4 (j % 4) .. +3.
+      const char* vrow = s_v + (4 * g4 + c16 / 4) * VSTR + 8 * (c16 & 3);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 vt = lds_read_tr_b16(vrow + 32 * dt);
+        o[dt] = MC::pv(vt, ph, o[dt]);
+        o[dt] = MC::pv(vt, pl, o[dt]);
+      }
+    };
+    auto consume = [&](auto rb, int u, int pb0, int pb1) __attribute__((always_inline)) {
+      constexpr int r = decltype(rb)::value;
+      const int nvalid = e_tok - 16 * u;
+      if (nvalid < 16 || (append && u == u_first + u_count - 1))
+        consume_t(std::true_type{}, kb[r], vb[r], u, nvalid, pb0, pb1);
+      else
+        consume_t(std::false_type{}, kb[r], vb[r], u, 16, pb0, pb1);
+    };
+
+    // Stream units first, first + stride, ... (< u_count) of the range, RING
+    // units in flight.  Every path into the steady-state loop has issued the
+    // same RING units (short windows repeat their last unit), so the waits
+    // the compiler places there are exact; the units left at the end of a
+    // window are consumed after the loop.  Table entries come 64 units at a
+    // time (lane k: the wavefront's k-th unit of the window); with `pre`, the
+    // first window's are already in pre_win / pre_win2.
+    auto stream_units = [&](int first, int stride, bool pre) __attribute__((always_inline)) {
+      const int nb = first < u_count ? (u_count - first + stride - 1) / stride : 0;
+      for (int j0 = 0; j0 < nb; j0 += kWave) {
+        const int jn = min(kWave, nb - j0);
+        auto unit_of = [&](int k) __attribute__((always_inline)) { return u_first + first + (j0 + k) * stride; };
+        int w0 = 0, w1 = 0;
+        if (pre && j0 == 0) {
+          w0 = pre_win;
+          w1 = pre_win2;
+        } else if (lane < jn) {
+          const int u = unit_of(lane);
+          w0 = tbl_row[BS == 8 ? 2 * u : (BS == 32 ? u >> 1 : u)];
+          if constexpr (BS == 8) w1 = tbl_row[min(2 * u + 1, last_blk)];
+        }
+        // Blocks of unit k; an 8-token unit's second block past the range
+        // (its entry may be unset) is replaced by its first (rows masked).
+        auto blocks = [&](int k, int& pb0, int& pb1) __attribute__((always_inline)) {
+          pb0 = uniform_lane(w0, k);
+          pb1 = pb0;
+          if constexpr (BS == 8) {
+            if (2 * unit_of(k) + 1 <= last_blk) pb1 = uniform_lane(w1, k);
+          }
+        };
+        auto iss = [&](auto rb, int k) __attribute__((always_inline)) {
+          int pb0, pb1;
+          blocks(k, pb0, pb1);
+          issue(rb, unit_of(k), pb0, pb1);
+        };
+        auto con = [&](auto rb, int k) __attribute__((always_inline)) {
+          int pb0, pb1;
+          blocks(k, pb0, pb1);
+          consume(rb, unit_of(k), pb0, pb1);
+        };
+        auto prologue = [&](auto rb) __attribute__((always_inline)) { iss(rb, min((int)decltype(rb)::value, jn - 1)); };
+        static_for<0, RING>(prologue);
+        int k = 0;
+        for (; k + RING < jn; k += RING) {
+          auto body = [&](auto rb) __attribute__((always_inline)) {
+            constexpr int r = decltype(rb)::value;
+            con(rb, k + r);
+            iss(rb, min(k + r + RING, jn - 1));
+          };
+          static_for<0, RING>(body);
+        }
+        auto tail = [&](auto rb) __attribute__((always_inline)) {
+          constexpr int r = decltype(rb)::value;
+          if (k + r < jn) con(rb, k + r);
+        };
+        static_for<0, RING>(tail);
+      }
+    };
+
+    if constexpr (FUSED) {
+      const int wstride = (int)gridDim.y * W;
+      const int p0 = (int)blockIdx.y * W + wave;
+      for (int p = p0; p < num_parts; p += wstride) {
+        set_range(p * chunk, min(ctx, (p + 1) * chunk));
+        stream_units(0, 1, p == p0);
+      }
+    } else {
+      set_range(tok_begin, tok_end);
+      stream_units(wave, W, true);
+    }
+
+    // The column's exp-sum over the four lane groups; then the wavefront's
+    // state goes to LDS, over the K/V tiles once every wavefront is done.
+    const float l_tot = xor32_sum(xor16_sum(l_part));
+    __syncthreads();
+    if (c16 < G) {
+      if (g4 == 0) {
+        s_m[wave][c16] = m_ref;
+        s_l[wave][c16] = l_tot;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(&s_acc[wave][c16][16 * dt + 4 * g4]) = o[dt];
+    }
+  } else {
+    // (Groups of four and eight take this path only where decode_uses_mfma
+    // sends them here; it stays complete for every group.)
+    // q pieces of the G heads of this group: in registers, or - for groups of
+    // four and more, whose accumulators take 32+ registers per lane - in LDS,
+    // read once per tile and head.
+    constexpr bool kQLds = G >= 4 && !kMfma;
+    __shared__ uint4 s_q[kQLds ? G : 1][kQLds ? D / 8 : 1];
+    uint32_t qv[kQLds ? 1 : G][4];
     if constexpr (kQLds) {
-      // Head by head, so only one head's q is live.
+      const uint16_t* qg = q + ((size_t)seq * num_q_heads + (size_t)kvh * G) * D;  // the group's G rows, contiguous
+      for (int t = threadIdx.x; t < G * D / 8; t += W * kWave)
+        s_q[t / (D / 8)][t % (D / 8)] = *reinterpret_cast<const uint4*>(qg + t * 8);
+      __syncthreads();
+    } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint4 qq = s_q[g][col];
+        const uint4 t = *reinterpret_cast<const uint4*>(q + ((size_t)seq * num_q_heads + kvh * G + g) * D + col * 8);
+        qv[g][0] = t.x; qv[g][1] = t.y; qv[g][2] = t.z; qv[g][3] = t.w;
+      }
+    }
+
+    float m[G], lsum[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = kNegBig;
+      lsum[g] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[g][d] = 0.f;
+    }
+
+    const size_t row_elems = (size_t)num_kv_heads * D;        // elements between consecutive slots
+    const size_t block_bytes = row_elems * kBlockSize * 2;    // bytes per physical block
+    // The streaming unit is a tile: TT consecutive slots of one block, LPBT
+    // wave loads per tensor (the whole block when it needs no more than
+    // tile_loads() loads), so the load buffers and per-token scores stay within
+    // the register budget for every head size, group and block size.
+    constexpr int LPBT = decode_tile_loads<D, G, BS>();
+    constexpr int TT = LPBT * TPL;  // slots per tile
+    constexpr int TPB = LPB / LPBT;  // tiles per block
+    const uint32_t tile_bytes = (uint32_t)(row_elems * TT * 2);
+    // Per-lane byte offset of load i inside a tile: slot (i*TPL + row), dims col*8.
+    uint32_t lane_off[LPBT];
+#pragma unroll
+    for (int i = 0; i < LPBT; ++i) lane_off[i] = (uint32_t)(((i * TPL + row) * row_elems + col * 8) * 2);
+    const char* kbase = reinterpret_cast<const char*>(k_cache) + (size_t)kvh * D * 2;
+    const char* vbase = reinterpret_cast<const char*>(v_cache) + (size_t)kvh * D * 2;
+
+    // The range being streamed: its blocks, the tokens in its last block, and
+    // whether it ends with the appended token.
+    int nblk = 0, last_valid = 0;
+    bool append = false;
+    const int32_t* tbl = block_tables;
+    auto set_range = [&](int b, int e) {
+      const int lb_begin = b / kBlockSize;
+      nblk = e > b ? (e - b + kBlockSize - 1) / kBlockSize : 0;
+      last_valid = e - (lb_begin + nblk - 1) * kBlockSize;
+      append = new_k != nullptr && ctx > 0 && e == ctx;
+      tbl = block_tables + (size_t)seq * max_blocks_per_seq + lb_begin;
+    };
+
+    // Loads of tile `sub` of physical block pb.
+    auto issue = [&](int pb, int sub, uint4 (&kk)[LPBT], uint4 (&vv)[LPBT]) {
+      const size_t off = (size_t)pb * block_bytes + (size_t)sub * tile_bytes;
+      const char* kb = kbase + off;
+      const char* vb = vbase + off;
+#pragma unroll
+      for (int i = 0; i < LPBT; ++i) kk[i] = load_nt16(kb + lane_off[i]);
+#pragma unroll
+      for (int i = 0; i < LPBT; ++i) vv[i] = load_nt16(vb + lane_off[i]);
+    };
+
+    // MASKED is only taken for tiles of the range's last block that hold slots
+    // past its last token (nvalid < TT; nvalid <= 0 masks the whole tile).
+    auto consume_t = [&](auto masked, const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int nvalid) {
+      constexpr bool MASKED = decltype(masked)::value;
+      float s[G][LPBT];
+      if constexpr (kQLds) {
+        // Head by head, so only one head's q is live.
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint4 qq = s_q[g][col];
+#pragma unroll
+          for (int i = 0; i < LPBT; ++i) {
+            const bool valid = !MASKED || (i * TPL + row) < nvalid;
+            float d = E::dot2(qq.x, kk[i].x, 0.f);
+            d = E::dot2(qq.y, kk[i].y, d);
+            d = E::dot2(qq.z, kk[i].z, d);
+            d = E::dot2(qq.w, kk[i].w, d);
+            d = group_sum<LPT>(d) * scale_log2;
+            s[g][i] = valid ? d : -INFINITY;
+          }
+        }
+      } else {
 #pragma unroll
         for (int i = 0; i < LPBT; ++i) {
           const bool valid = !MASKED || (i * TPL + row) < nvalid;
-          float d = E::dot2(qq.x, kk[i].x, 0.f);
-          d = E::dot2(qq.y, kk[i].y, d);
-          d = E::dot2(qq.z, kk[i].z, d);
-          d = E::dot2(qq.w, kk[i].w, d);
-          d = group_sum<LPT>(d) * scale_log2;
-          s[g][i] = valid ? d : -INFINITY;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = E::dot2(qv[g][0], kk[i].x, 0.f);
+            d = E::dot2(qv[g][1], kk[i].y, d);
+            d = E::dot2(qv[g][2], kk[i].z, d);
+            d = E::dot2(qv[g][3], kk[i].w, d);
+            d = group_sum<LPT>(d) * scale_log2;
+            s[g][i] = valid ? d : -INFINITY;
+          }
         }
       }
-    } else {
+      float p[G][LPBT];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = m[g];
+#pragma unroll
+        for (int i = 0; i < LPBT; ++i) mx = fmaxf(mx, s[g][i]);
+        const float alpha = fast_exp2(m[g] - mx);
+        m[g] = mx;
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < LPBT; ++i) {
+          p[g][i] = fast_exp2(s[g][i] - mx);
+          ps += p[g][i];
+        }
+        lsum[g] = lsum[g] * alpha + ps;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
+      }
 #pragma unroll
       for (int i = 0; i < LPBT; ++i) {
         const bool valid = !MASKED || (i * TPL + row) < nvalid;
+        const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+        float vf[8];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = E::dot2(qv[g][0], kk[i].x, 0.f);
-          d = E::dot2(qv[g][1], kk[i].y, d);
-          d = E::dot2(qv[g][2], kk[i].z, d);
-          d = E::dot2(qv[g][3], kk[i].w, d);
-          d = group_sum<LPT>(d) * scale_log2;
-          s[g][i] = valid ? d : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          vf[2 * e] = E::lo(w4[e]);
+          vf[2 * e + 1] = E::hi(w4[e]);
         }
+        if (MASKED && !valid) {
+#pragma unroll
+          for (int d = 0; d < 8; ++d) vf[d] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[g][d] = fmaf(p[g][i], vf[d], acc[g][d]);
+      }
+    };
+
+    // Tile `sub` of the range's block blk (physical id pb, used only for the
+    // appended token's store).
+    auto consume = [&](const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int blk, int sub, int pb) {
+      const bool last = blk == nblk - 1;
+      const int nvalid = last ? last_valid - sub * TT : TT;
+      const int r = last_valid - 1 - sub * TT;  // the appended slot's row in this tile, if in [0, TT)
+      if (last && append && r >= 0 && r < TT) {
+        // Load i = r / TPL, lane row r % TPL holds the appended token.
+        uint4 ka2[LPBT], va2[LPBT];
+#pragma unroll
+        for (int i = 0; i < LPBT; ++i) {
+          const bool mine = i * TPL + row == r;
+          ka2[i] = mine ? app_k : kk[i];
+          va2[i] = mine ? app_v : vv[i];
+        }
+        if (row == r % TPL) {
+          const size_t off = (size_t)kvh * D * 2 + (size_t)pb * block_bytes + (size_t)sub * tile_bytes + lane_off[0] +
+                             (size_t)((r / TPL) * TPL) * row_elems * 2;
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + off) = app_k;
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + off) = app_v;
+        }
+        if (nvalid < TT)
+          consume_t(std::true_type{}, ka2, va2, nvalid);
+        else
+          consume_t(std::false_type{}, ka2, va2, TT);
+      } else if (nvalid < TT) {
+        consume_t(std::true_type{}, kk, vv, nvalid);
+      } else {
+        consume_t(std::false_type{}, kk, vv, TT);
+      }
+    };
+
+    // Stream the tiles of blocks first, first + stride, ... (< nblk) of the
+    // range: double buffered, so while a tile is consumed the next one's
+    // 2*LPBT loads are in flight.  Every path into the steady-state body has
+    // issued the same two tiles' loads (a one-tile window loads its tile
+    // twice), so the waits the compiler places there are exact: each consume
+    // waits for its own loads only, never for the tile behind it.  The 1-3
+    // tiles left at the end of a window are peeled (their waits may be
+    // conservative).  Table entries come 64 at a time (lane k holds the entry
+    // of the wave's block j0 + k); with `pre`, the first window's are already
+    // in pre_win.  Tile u of a window is tile u % TPB of its block u / TPB.
+    auto stream_blocks = [&](int first, int stride, bool pre) {
+      const int nb = first < nblk ? (nblk - first + stride - 1) / stride : 0;
+      uint4 ka[LPBT], va[LPBT], kb2[LPBT], vb2[LPBT];
+      for (int j0 = 0; j0 < nb; j0 += kWave) {
+        const int jn = min(kWave, nb - j0);
+        const int tbl_win = pre && j0 == 0 ? pre_win : (lane < jn ? tbl[first + (j0 + lane) * stride] : 0);
+        const int blk_base = first + j0 * stride;  // range-relative index of the window's block 0
+        const int nt = jn * TPB;
+        auto pb_of = [&](int u) { return uniform_lane(tbl_win, u / TPB); };
+        auto blk_of = [&](int u) { return blk_base + (u / TPB) * stride; };
+        issue(pb_of(0), 0, ka, va);
+        const int u1 = nt > 1 ? 1 : 0;
+        issue(pb_of(u1), u1 % TPB, kb2, vb2);
+        int u = 0;
+        for (; u + 3 < nt; u += 2) {
+          consume(ka, va, blk_of(u), u % TPB, pb_of(u));
+          issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
+          consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
+          issue(pb_of(u + 3), (u + 3) % TPB, kb2, vb2);
+        }
+        const int rem = nt - u;  // 1, 2 or 3 tiles left; ka holds u, kb2 holds u + 1
+        consume(ka, va, blk_of(u), u % TPB, pb_of(u));
+        if (rem == 3) issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
+        if (rem >= 2) consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
+        if (rem == 3) consume(ka, va, blk_of(u + 2), (u + 2) % TPB, pb_of(u + 2));
+      }
+    };
+
+    if constexpr (FUSED) {
+      // This wavefront's chunks, one running state over all of them.
+      const int wstride = (int)gridDim.y * W;
+      const int p0 = (int)blockIdx.y * W + wave;
+      for (int p = p0; p < num_parts; p += wstride) {
+        set_range(p * chunk, min(ctx, (p + 1) * chunk));
+        stream_blocks(0, 1, p == p0);
+      }
+    } else {
+      set_range(tok_begin, tok_end);
+      stream_blocks(wave, W, true);
+    }
+
+    // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(m[g], off);
+        const float lo = __shfl_xor(lsum[g], off);
+        const float mm = fmaxf(m[g], mo);
+        const float fa = fast_exp2(m[g] - mm);
+        const float fb = fast_exp2(mo - mm);
+        lsum[g] = lsum[g] * fa + lo * fb;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[g][d] = acc[g][d] * fa + __shfl_xor(acc[g][d], off) * fb;
+        m[g] = mm;
       }
     }
-    float p[G][LPBT];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
-#pragma unroll
-      for (int i = 0; i < LPBT; ++i) mx = fmaxf(mx, s[g][i]);
-      const float alpha = fast_exp2(m[g] - mx);
-      m[g] = mx;
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < LPBT; ++i) {
-        p[g][i] = fast_exp2(s[g][i] - mx);
-        ps += p[g][i];
-      }
-      lsum[g] = lsum[g] * alpha + ps;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[g][d] *= alpha;
-    }
-#pragma unroll
-    for (int i = 0; i < LPBT; ++i) {
-      const bool valid = !MASKED || (i * TPL + row) < nvalid;
-      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-      float vf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = E::lo(w4[e]);
-        vf[2 * e + 1] = E::hi(w4[e]);
-      }
-      if (MASKED && !valid) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) vf[d] = 0.f;
-      }
+
+    // The wavefront's state to LDS.
+    if (row == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[g][d] = fmaf(p[g][i], vf[d], acc[g][d]);
+        for (int d = 0; d < 8; ++d) s_acc[wave][g][col * 8 + d] = acc[g][d];
     }
-  };
-
-  // Tile `sub` of the range's block blk (physical id pb, used only for the
-  // appended token's store).
-  auto consume = [&](const uint4 (&kk)[LPBT], const uint4 (&vv)[LPBT], int blk, int sub, int pb) {
-    const bool last = blk == nblk - 1;
-    const int nvalid = last ? last_valid - sub * TT : TT;
-    const int r = last_valid - 1 - sub * TT;  // the appended slot's row in this tile, if in [0, TT)
-    if (last && append && r >= 0 && r < TT) {
-      // Load i = r / TPL, lane row r % TPL holds the appended token.
-      uint4 ka2[LPBT], va2[LPBT];
+    if (lane == 0) {
 #pragma unroll
-      for (int i = 0; i < LPBT; ++i) {
-        const bool mine = i * TPL + row == r;
-        ka2[i] = mine ? app_k : kk[i];
-        va2[i] = mine ? app_v : vv[i];
+      for (int g = 0; g < G; ++g) {
+        s_m[wave][g] = m[g];
+        s_l[wave][g] = lsum[g];
       }
-      if (row == r % TPL) {
-        const size_t off = (size_t)kvh * D * 2 + (size_t)pb * block_bytes + (size_t)sub * tile_bytes + lane_off[0] +
-                           (size_t)((r / TPL) * TPL) * row_elems * 2;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(k_store) + off) = app_k;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(v_store) + off) = app_v;
-      }
-      if (nvalid < TT)
-        consume_t(std::true_type{}, ka2, va2, nvalid);
-      else
-        consume_t(std::false_type{}, ka2, va2, TT);
-    } else if (nvalid < TT) {
-      consume_t(std::true_type{}, kk, vv, nvalid);
-    } else {
-      consume_t(std::false_type{}, kk, vv, TT);
-    }
-  };
-
-  // Stream the tiles of blocks first, first + stride, ... (< nblk) of the
-  // range: double buffered, so while a tile is consumed the next one's
-  // 2*LPBT loads are in flight.  Every path into the steady-state body has
-  // issued the same two tiles' loads (a one-tile window loads its tile
-  // twice), so the waits the compiler places there are exact: each consume
-  // waits for its own loads only, never for the tile behind it.  The 1-3
-  // tiles left at the end of a window are peeled (their waits may be
-  // conservative).  Table entries come 64 at a time (lane k holds the entry
-  // of the wave's block j0 + k); with `pre`, the first window's are already
-  // in pre_win.  Tile u of a window is tile u % TPB of its block u / TPB.
-  auto stream_blocks = [&](int first, int stride, bool pre) {
-    const int nb = first < nblk ? (nblk - first + stride - 1) / stride : 0;
-    uint4 ka[LPBT], va[LPBT], kb2[LPBT], vb2[LPBT];
-    for (int j0 = 0; j0 < nb; j0 += kWave) {
-      const int jn = min(kWave, nb - j0);
-      const int tbl_win = pre && j0 == 0 ? pre_win : (lane < jn ? tbl[first + (j0 + lane) * stride] : 0);
-      const int blk_base = first + j0 * stride;  // range-relative index of the window's block 0
-      const int nt = jn * TPB;
-      auto pb_of = [&](int u) { return uniform_lane(tbl_win, u / TPB); };
-      auto blk_of = [&](int u) { return blk_base + (u / TPB) * stride; };
-      issue(pb_of(0), 0, ka, va);
-      const int u1 = nt > 1 ? 1 : 0;
-      issue(pb_of(u1), u1 % TPB, kb2, vb2);
-      int u = 0;
-      for (; u + 3 < nt; u += 2) {
-        consume(ka, va, blk_of(u), u % TPB, pb_of(u));
-        issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
-        consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
-        issue(pb_of(u + 3), (u + 3) % TPB, kb2, vb2);
-      }
-      const int rem = nt - u;  // 1, 2 or 3 tiles left; ka holds u, kb2 holds u + 1
-      consume(ka, va, blk_of(u), u % TPB, pb_of(u));
-      if (rem == 3) issue(pb_of(u + 2), (u + 2) % TPB, ka, va);
-      if (rem >= 2) consume(kb2, vb2, blk_of(u + 1), (u + 1) % TPB, pb_of(u + 1));
-      if (rem == 3) consume(ka, va, blk_of(u + 2), (u + 2) % TPB, pb_of(u + 2));
-    }
-  };
-
-  if constexpr (FUSED) {
-    // This wavefront's chunks, one running state over all of them.
-    const int wstride = (int)gridDim.y * W;
-    const int p0 = (int)blockIdx.y * W + wave;
-    for (int p = p0; p < num_parts; p += wstride) {
-      set_range(p * chunk, min(ctx, (p + 1) * chunk));
-      stream_blocks(0, 1, p == p0);
-    }
-  } else {
-    set_range(tok_begin, tok_end);
-    stream_blocks(wave, W, true);
-  }
-
-  // Merge the rows of this wavefront (butterfly over lane ^ LPT, ^ 2 LPT, ...).
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(lsum[g], off);
-      const float mm = fmaxf(m[g], mo);
-      const float fa = fast_exp2(m[g] - mm);
-      const float fb = fast_exp2(mo - mm);
-      lsum[g] = lsum[g] * fa + lo * fb;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[g][d] = acc[g][d] * fa + __shfl_xor(acc[g][d], off) * fb;
-      m[g] = mm;
     }
   }
 
   // Merge the wavefronts through LDS, normalise and store.
-  __shared__ float s_m[W][G], s_l[W][G];
-  __shared__ float s_acc[W][G][D];
-  if (row == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) s_acc[wave][g][col * 8 + d] = acc[g][d];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = m[g];
-      s_l[wave][g] = lsum[g];
-    }
-  }
   __syncthreads();
   for (int t = threadIdx.x; t < G * D; t += W * kWave) {
     const int g = t / D, d = t % D;
@@ -805,6 +1170,7 @@ constexpr int kSplitWaves = PKA_SPLIT_WAVES;    // wavefronts per split-K partit
 // may use the accumulation registers as well.
 template <int D, int G, int BS>
 constexpr int fused_waves() {
+  if (decode_uses_mfma<G>()) return 4;  // the matrix-core path's ring of loads fills the register budget
   return 16 * decode_tile_loads<D, G, BS>() + 12 * G <= 100 ? 8 : 4;
 }
 // Heavy-first ordering scans all context lengths in every workgroup; above
