@@ -159,7 +159,9 @@ struct McGeom {
   static constexpr int VSTR = 2 * D + 32;      // LDS row stride of the V tile, bytes
   static constexpr int TILE = 16 * (KSTR + VSTR);  // one wavefront's K and V tiles
   // Units whose loads are in flight at once (registers: 8 * NL per unit).
-  static constexpr int RING = D == 64 ? 4 : 2;
+  // Two: measured at 64 dims, rings of three and four units cost occupancy
+  // (three and four wavefronts per SIMD against four) and ran 2-4 % slower.
+  static constexpr int RING = 2;
 };
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
