@@ -30,8 +30,11 @@ def bits(t):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["write+decode", "decode_append"])
 @pytest.mark.parametrize("ctx", [[300, 1500, 77, 2000], [4000, 9000]], ids=["single-pass", "split-k"])
-def test_graph_replay_matches_oracle(pka, ctx, fused):
-    step = W.make_decode_step(context_lens=ctx, dtype=torch.bfloat16, num_q_heads=16, num_kv_heads=8, head_dim=128,
+@pytest.mark.parametrize("hq", [16, 64], ids=["group2", "group8"])
+def test_graph_replay_matches_oracle(pka, ctx, fused, hq):
+    """Groups of two run on the vector path, groups of eight on the matrix
+    cores; both are captured and replayed."""
+    step = W.make_decode_step(context_lens=ctx, dtype=torch.bfloat16, num_q_heads=hq, num_kv_heads=8, head_dim=128,
                               seed=41, poison=True, write_new=True)
     ds = DevStep(step)
     S, Hq, D = step.q.shape
@@ -51,7 +54,7 @@ def test_graph_replay_matches_oracle(pka, ctx, fused):
         pka.paged_attn_decode(ds.q, ds.k_cache, ds.v_cache, ds.block_tables, ds.context_lens, step.scale, max_ctx,
                               out=out, workspace=ws)
 
-    say(f"graph capture of the decode step, ctx={ctx}, fused={fused}, "
+    say(f"graph capture of the decode step, ctx={ctx}, fused={fused}, Hq={hq}, "
         f"variant={pka.decode_choose_variant(S, step.num_kv_heads, max_ctx)}")
     eager = torch.empty_like(ds.q)
     run(eager)

@@ -84,6 +84,19 @@ def test_noalloc_single_pass_then_smaller(pka):
     assert _check_case(pka, step, "smaller single-pass batch") == 1
 
 
+def test_noalloc_group8_split_then_single(pka):
+    """Groups of eight (the matrix-core path): a split-K batch, then a
+    single-pass batch, both through the scratch-free entry point."""
+    step = W.make_decode_step(context_lens=[9000, 40, 5000], dtype=torch.bfloat16, num_q_heads=64, num_kv_heads=8,
+                              head_dim=128, seed=53, poison=True)
+    assert _check_case(pka, step, "group-8 split-K batch") == 2
+    g = torch.Generator().manual_seed(54)
+    ctx = torch.randint(100, 2049, (300,), generator=g).tolist()
+    step = W.make_decode_step(context_lens=ctx, dtype=torch.bfloat16, num_q_heads=64, num_kv_heads=8, head_dim=128,
+                              seed=54, poison=True)
+    assert _check_case(pka, step, "group-8 single-pass batch") == 1
+
+
 def test_noalloc_refuses_beyond_scratch(pka):
     """A split-K request whose partition states exceed the built-in scratch is
     refused with PKA_ERR_SCRATCH before anything is launched (the pointers are
