@@ -56,8 +56,8 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # source of its traffic figure, or why it is null.
 TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode_impl.h", "11e5a0bd772e7142", 1191837594),
-    "splitk": ("decode_impl.h", "11e5a0bd772e7142", 269528883),
+    "decode_step": ("decode_impl.h", "6896da5d79401c76", 1191836812),
+    "splitk": ("decode_impl.h", "6896da5d79401c76", 269528730),
     "mixed": ("prefill.hip", "f3a7a434c9bc9410", 50191565),
     "prefill_long": ("prefill.hip", "f3a7a434c9bc9410", 319682867),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),

@@ -66,9 +66,10 @@ struct DecodeLayout {
   static_assert(kWave % LPT == 0 && BS % TPL == 0 && kPartitionSize % BS == 0, "unsupported head_dim / block");
 };
 
-// Wave loads per tensor in one streaming tile (see paged_decode_kernel): the
-// whole block up to four loads (two for groups of eight query heads, whose
-// accumulators and scores take twice the registers of a group of four).
+// Wave loads per tensor in one streaming tile of the vector path (see
+// paged_decode_kernel): the whole block up to four loads (two for groups of
+// eight query heads, whose accumulators and scores take twice the registers
+// of a group of four).
 template <int D, int G, int BS>
 constexpr int decode_tile_loads() {
   constexpr int cap = G >= 8 ? 2 : 4;
@@ -158,9 +159,10 @@ struct McGeom {
   static constexpr int KSTR = 2 * D + 16;      // LDS row stride of the K tile, bytes
   static constexpr int VSTR = 2 * D + 32;      // LDS row stride of the V tile, bytes
   static constexpr int TILE = 16 * (KSTR + VSTR);  // one wavefront's K and V tiles
-  // Units whose loads are in flight at once (registers: 8 * NL per unit).
-  // Two: measured at 64 dims, rings of three and four units cost occupancy
-  // (three and four wavefronts per SIMD against four) and ran 2-4 % slower.
+  // Register buffers of the load ring (8 * NL registers each): while one
+  // unit is computed, the next one's loads are in flight.  Two: measured at
+  // 64 dims, rings of three and four cost occupancy (three and four
+  // wavefronts per SIMD against four) and ran 2-4 % slower.
   static constexpr int RING = 2;
 };
 
