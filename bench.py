@@ -18,8 +18,10 @@ Other workloads (--workload): `splitk` (4 x 16,384-token split-K decode),
 `sweep` (single-request fp16 decode at 128 / 1,024 / 4,096 tokens, next to a
 materialise-then-attend arm), `single` (the 128-token request alone),
 `prefill_long` (4 x 2,048 causal rows after 6,144 cached tokens), `shapes`
-(the decode batch at other head / group / block shapes), `rope_kv_write`,
-`block_manager`, `copy` (a device copy, for counter calibration).
+(the decode batch at other head / group / block shapes), `prefill_shapes`
+(the long prefill's chunks at other head / group / block shapes),
+`rope_kv_write`, `block_manager`, `copy` (a device copy, for counter
+calibration).
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  Pools are rotated over several device copies so no step reads what
@@ -58,8 +60,8 @@ TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
     "decode_step": ("decode_impl.h", "6896da5d79401c76", 1191836812),
     "splitk": ("decode_impl.h", "6896da5d79401c76", 269528730),
-    "mixed": ("prefill.hip", "f3a7a434c9bc9410", 50191565),
-    "prefill_long": ("prefill.hip", "f3a7a434c9bc9410", 319682867),
+    "mixed": ("prefill.hip", "36bd19136b2a940f", 50191451),
+    "prefill_long": ("prefill.hip", "36bd19136b2a940f", 319749208),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),
 }
 
@@ -90,7 +92,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_step",
                    choices=["decode_step", "splitk", "mixed", "sweep", "single", "copy", "rope_kv_write",
-                            "block_manager", "prefill_long", "shapes"])
+                            "block_manager", "prefill_long", "shapes", "prefill_shapes"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--settle-ms", type=float, default=500.0,
                    help="untimed stepping before the first timed block (clock/power ramp), once per process")
@@ -756,6 +758,73 @@ def bench_prefill_long(args, pka):
     return res, None, False
 
 
+# (label, dtype, Hq, Hkv, head_dim, block) of the prefill shape rows: the
+# long prefill's chunks (4 x 2,048 rows after 6,144 cached) at other head,
+# group and block shapes.
+PREFILL_SHAPES = [
+    ("G2 d128 b16 (16q/8kv)", torch.bfloat16, 16, 8, 128, 16),
+    ("G8 d128 b16 (32q/4kv)", torch.bfloat16, 32, 4, 128, 16),
+    ("G4 d128 b32 (32q/8kv)", torch.bfloat16, 32, 8, 128, 32),
+    ("G1 d128 b16 (16q/16kv, fp16)", torch.float16, 16, 16, 128, 16),
+    ("G2 d64 b16 (32q/16kv)", torch.bfloat16, 32, 16, 64, 16),
+    ("G2 d256 b8 (8q/4kv)", torch.bfloat16, 8, 4, 256, 8),
+]
+
+
+def bench_prefill_shapes(args, pka):
+    """The prefill on the long prefill's chunks at each of PREFILL_SHAPES:
+    us per call (events around each call) and algorithmic TFLOP/s."""
+    ql, cached = [2048] * 4, [6144] * 4
+    dev = torch.device("cuda:0")
+    rows = {}
+    first = None
+    for label, dtype, hq, hkv, d, bs in PREFILL_SHAPES:
+        step = W.make_prefill_step(query_lens=ql, cached_lens=cached, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                                   head_dim=d, block_size=bs, seed=args.seed, poison=False, write_new=False)
+        k, v, q = step.k_cache.to(dev), step.v_cache.to(dev), step.q.to(dev)
+        bt, cl, qsl = step.block_tables.to(dev), step.context_lens.to(dev), step.query_start_loc.to(dev)
+        out = torch.empty_like(q)
+        mcl = int(step.context_lens.max())
+        ws = pka.prefill_workspace(step.num_prefill, step.num_prefill_rows, hq, hkv, d, mcl, dev)
+        run = pka.paged_attn_prefill(q, k, v, bt, cl, qsl, step.scale, step.max_query_len, mcl, out=out,
+                                     workspace=ws, prepare=True)
+
+        def launch(i, ev):
+            if ev:
+                ev[0].record()
+            run()
+            if ev:
+                ev[1].record()
+
+        st = {}
+        _, (pre_ms,) = timed_loop(launch, 1, args.steps, args.warmup, stats=st)
+        flops = W.prefill_flops(step)
+        tflops = flops / (pre_ms * 1e-3) / 1e12
+        rows[label] = {"us_per_call": round(pre_ms * 1e3, 2), "us_p10_p50_p90": [round(x * 1e3, 2) for x in st["pct"][0]],
+                       "algorithmic_flops": flops, "TFLOPs": round(tflops, 1),
+                       "pct_of_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 1)}
+        log(f"{label}: {rows[label]['us_per_call']} us, {rows[label]['TFLOPs']} TFLOP/s")
+        if first is None:
+            first = (label, pre_ms, tflops)
+        del k, v, q, out, ws, run
+        torch.cuda.empty_cache()
+    label, pre_ms, tflops = first
+    return {
+        "metric": "paged prefill TFLOP/s (bf16 MFMA, algorithmic FLOPs), 1 MI355X",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(pre_ms, 4),
+        "per_shape": rows,
+        "dtype": "bf16",
+        "config": {"workload": "paged prefill: 4 chunks of 2,048 rows after 6,144 cached tokens each, per "
+                               "head/group/block shape; value: " + label, "seed": args.seed},
+        "roofline": {"kernel": f"paged_prefill_kernel ({label})", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }, None, False
+
+
 def cpu_baseline_prefill(step, budget_s):
     """The oracle (as is) on a sample of the workload: rows of chunk 0 (each
     sees the 6,144 cached keys plus its causal prefix), as many as the budget
@@ -1237,6 +1306,8 @@ def main():
         res, step, write = bench_prefill_long(args, pka)
     elif args.workload == "shapes":
         res, step, write = bench_shapes(args, pka)
+    elif args.workload == "prefill_shapes":
+        res, step, write = bench_prefill_shapes(args, pka)
     else:
         raise SystemExit(f"workload {args.workload} is not available yet")
 

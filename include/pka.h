@@ -334,7 +334,7 @@ size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32
  * more than this is split), or -1 for invalid sizes.  Host function, for
  * callers and tests that want to know where the split boundaries fall. */
 int32_t pka_prefill_split_keys(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t max_context_len);
+                               int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 
 /* Number of compute units of the current device (cached per device after the
  * first call), or a negative value if the HIP runtime fails. */

@@ -98,7 +98,7 @@ _SIGNATURES = {
          c_int32, c_float, c_void_p, CacheDesc, c_void_p, c_size_t, c_void_p],
     ),
     "pka_prefill_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
-    "pka_prefill_split_keys": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pka_prefill_split_keys": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pka_rope_table": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_double, c_void_p]),
     "pka_rope_table_bytes": (c_size_t, [c_int32, c_int32]),
     "pka_bm_create": (c_void_p, [c_int32, c_int32]),
@@ -554,9 +554,9 @@ def prefill_workspace(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_di
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def prefill_split_keys(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, max_context_len) -> int:
+def prefill_split_keys(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
     """Keys per split the prefill launch uses for these sizes on the current device."""
-    n = int(lib.pka_prefill_split_keys(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, max_context_len))
+    n = int(lib.pka_prefill_split_keys(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len))
     if n < 0:
         raise ValueError("invalid prefill sizes")
     return n

@@ -421,19 +421,19 @@ size_t pka_prefill_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32
       max_context_len <= 0 || num_q_heads % num_kv_heads)
     return 0;
   const int group = num_q_heads / num_kv_heads;
-  const int keys = pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, group, max_context_len,
+  const int keys = pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, group, head_dim, max_context_len,
                                            pka_device_cu_count());
   return pka::prefill_workspace_floats(num_q_tokens, num_seqs, num_kv_heads, group, head_dim, max_context_len, keys) *
          sizeof(float);
 }
 
 int32_t pka_prefill_split_keys(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0 ||
-      num_q_heads % num_kv_heads)
+                               int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0 || num_q_heads % num_kv_heads)
     return -1;
-  return pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, num_q_heads / num_kv_heads, max_context_len,
-                                 pka_device_cu_count());
+  return pka::prefill_split_keys(num_q_tokens, num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim,
+                                 max_context_len, pka_device_cu_count());
 }
 
 int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -481,8 +481,8 @@ int32_t pka_paged_attn_prefill(const void* q, const void* k_cache, const void* v
   a.scale = scale;
   a.bf16 = cache.dtype == PKA_BF16;
   a.out = static_cast<uint16_t*>(out);
-  a.split_keys = pka::prefill_split_keys(num_q_tokens, num_seqs, cache.num_kv_heads, group, max_context_len,
-                                         pka_device_cu_count());
+  a.split_keys = pka::prefill_split_keys(num_q_tokens, num_seqs, cache.num_kv_heads, group, cache.head_dim,
+                                         max_context_len, pka_device_cu_count());
   a.workspace = need > 0 ? static_cast<float*>(workspace) : nullptr;
   return hip_status(pka::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }

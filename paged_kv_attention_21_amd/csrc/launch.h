@@ -131,7 +131,7 @@ hipError_t launch_rope_table(float* table, int max_position, int head_dim, doubl
 hipError_t launch_rope_kv_write(const RopeKvArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 bool prefill_supported(bool bf16, int head_dim, int group, int block_size);
-int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int max_context_len,
+int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim, int max_context_len,
                        int num_cus);
 size_t prefill_workspace_floats(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
                                 int max_context_len, int split_keys);

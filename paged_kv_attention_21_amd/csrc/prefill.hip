@@ -843,18 +843,20 @@ size_t prefill_tiles_upper_bound(int num_q_tokens, int num_seqs, int group) {
 // Keys per split.  Splitting a query tile's key range buys parallelism at
 // the price of writing and merging a partial state per split, so it is used
 // only to fill the GPU: the number of (query tile, KV head) work items is
-// multiplied by the smallest split count that gives about four per compute
-// unit (two rounds of two resident workgroups), and no split is shorter than
-// kPfMinSplitKeys keys.  Batches with enough query tiles are not split at all.
+// multiplied by the smallest split count that gives about two rounds of
+// resident workgroups per compute unit (four items up to 128 dims, two at 256
+// dims, whose workgroups take a whole compute unit's LDS), and no split is
+// shorter than kPfMinSplitKeys keys.  Batches with enough query tiles are not split at all.
 // The host sees only the longest context, not how the work spreads over the
 // chunks: when one long chunk shares a batch with short ones, its splits set
 // the critical path, so splits are held to kPfCapSplitKeys keys unless that
 // would more than double the work-item target (a batch of uniformly long
 // chunks, where longer splits cost less than the extra partial states).
-int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int max_context_len,
-                       int num_cus) {
+int prefill_split_keys(int num_q_tokens, int num_seqs, int num_kv_heads, int group, int head_dim,
+                       int max_context_len, int num_cus) {
   const size_t items = prefill_tiles_upper_bound(num_q_tokens, num_seqs, group) * (size_t)num_kv_heads;
-  const size_t target = 4 * (size_t)(num_cus > 0 ? num_cus : 256);
+  const size_t per_cu = head_dim > 128 ? 2 : 4;  // two rounds of the workgroups one compute unit holds
+  const size_t target = per_cu * (size_t)(num_cus > 0 ? num_cus : 256);
   size_t s = items >= target ? 1 : (target + items - 1) / items;
   s = std::min(s, (size_t)std::max(1, (max_context_len + kPfMinSplitKeys - 1) / kPfMinSplitKeys));
   int keys = (int)(((size_t)max_context_len + s - 1) / s);

@@ -127,34 +127,39 @@ def test_prefill_validation(pka):
     assert pka.prefill_workspace_bytes(4, 8192, 16, 8, 128, 8192) == 0
 
 
-def _prefill_splits(num_seqs, num_q_tokens, hkv, group, max_ctx, cus=256):
+def _prefill_splits(num_seqs, num_q_tokens, hkv, group, max_ctx, d=128, cus=256):
     """The split count the library's policy gives (restated from its
-    definition: about four (query tile, KV head) items per compute unit,
-    splits of at least 256 keys and, in batches where that keeps the items
-    within twice the target, of at most 1,024; whole 64-key tiles)."""
+    definition: about four (query tile, KV head) items per compute unit - two
+    at head size 256, whose workgroups take a whole compute unit -, splits of
+    at least 256 keys and, in batches where that keeps the items within twice
+    the target, of at most 1,024; whole 64-key tiles)."""
     tiles = -(-num_q_tokens // (128 // group)) + num_seqs
     items = tiles * hkv
-    s = 1 if items >= 4 * cus else -(-4 * cus // items)
+    target = (2 if d > 128 else 4) * cus
+    s = 1 if items >= target else -(-target // items)
     s = min(s, max(1, -(-max_ctx // 256)))
     keys = -(-max_ctx // s)
-    if s > 1 and keys > 1024 and items * -(-max_ctx // 1024) <= 8 * cus:
+    if s > 1 and keys > 1024 and items * -(-max_ctx // 1024) <= 2 * target:
         keys = 1024
     keys = max(64, -(-keys // 64) * 64)
     return -(-max_ctx // keys), tiles
 
 
-@pytest.mark.parametrize("shape", [(2, 10, 8, 2, 5000), (5, 1984, 8, 2, 3072), (5, 1984, 8, 2, 5632),
-                                   (4, 2048, 8, 2, 16896),
-                                   (1, 7, 2, 1, 4096), (8, 4096, 8, 2, 8192), (3, 300, 4, 4, 700)])
+@pytest.mark.parametrize("shape", [(2, 10, 8, 2, 5000, 128), (5, 1984, 8, 2, 3072, 128), (5, 1984, 8, 2, 5632, 128),
+                                   (4, 2048, 8, 2, 16896, 128),
+                                   (1, 7, 2, 1, 4096, 128), (8, 4096, 8, 2, 8192, 128), (3, 300, 4, 4, 700, 128),
+                                   (4, 8192, 4, 2, 8192, 256), (4, 8192, 4, 2, 8192, 128), (2, 600, 4, 2, 3000, 256),
+                                   (3, 300, 4, 4, 700, 64)])
 def test_prefill_split_policy(pka, shape):
     """The workspace the library asks for is the split states of exactly the
-    split count the policy gives (CPU: the 256-CU default)."""
-    ns, nq, hkv, g, ctx = shape
-    d = 128
-    splits, tiles = _prefill_splits(ns, nq, hkv, g, ctx)
+    split count the policy gives (CPU: the 256-CU default).  The long prefill
+    at head size 256 with 4 KV heads fills two rounds of one workgroup per
+    compute unit unsplit; at 128 dims the same batch is split in two."""
+    ns, nq, hkv, g, ctx, d = shape
+    splits, tiles = _prefill_splits(ns, nq, hkv, g, ctx, d)
     want = 0 if splits <= 1 else tiles * splits * hkv * 128 * (d + 2) * 4
     assert pka.prefill_workspace_bytes(ns, nq, hkv * g, hkv, d, ctx) == want
-    keys = pka.prefill_split_keys(ns, nq, hkv * g, hkv, ctx)
+    keys = pka.prefill_split_keys(ns, nq, hkv * g, hkv, d, ctx)
     assert keys % 64 == 0 and -(-ctx // keys) == splits
 
 

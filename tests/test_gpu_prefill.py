@@ -73,7 +73,7 @@ def test_long_context_splits(pka, shape):
     chunk sizes, the split length the launch picks)."""
     dtype, hq, hkv, d = shape
     ql = [64, 65, 128, 1, 300, 17]
-    keys = pka.prefill_split_keys(len(ql), sum(ql), hq, hkv, 7680)
+    keys = pka.prefill_split_keys(len(ql), sum(ql), hq, hkv, d, 7680)
     say(f"split length {keys} keys")
     bq = 128 // (hq // hkv)  # query positions per tile
     # first tile of chunk 0 ends at keys, of chunk 1 at keys + 1; chunk 5 ends at 2 * keys
@@ -226,7 +226,7 @@ def test_long_prefill_bench_size_sampled_rows(pka):
     mcl = int(step.prefill_context_lens.max())
     ws = torch.empty(max(1, pka.prefill_workspace_bytes(step.num_prefill, step.num_prefill_rows, Hq, Hkv, D, mcl)),
                      dtype=torch.uint8, device="cuda")
-    say(f"long prefill at bench size: split length {pka.prefill_split_keys(4, 8192, Hq, Hkv, mcl)} keys")
+    say(f"long prefill at bench size: split length {pka.prefill_split_keys(4, 8192, Hq, Hkv, D, mcl)} keys")
     out = pka.paged_attn_prefill(ds.prefill_q, ds.k_cache, ds.v_cache, ds.prefill_block_tables,
                                  ds.prefill_context_lens, ds.query_start_loc, step.scale, step.max_query_len, mcl,
                                  out=None, workspace=ws)
