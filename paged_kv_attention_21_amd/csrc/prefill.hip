@@ -697,6 +697,11 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const uint16_t* kt_lds = lds + (t & 1) * LD::STAGE;
     const uint16_t* vt_lds = kt_lds + LD::TILE;
     uint16_t* next = lds + ((t + 1) & 1) * LD::STAGE;
+    // Scheduler hint: interleave the tile's MFMAs with its exp work (the
+    // compiler's strategy for softmax-between-products loops).  Measured:
+    // long prefill 1,012 -> 1,019-1,021 TFLOP/s, mixed-step prefill call
+    // 40.1-40.3 -> 39.3 us; strategies 0 and 2 gain about the same.
+    __builtin_amdgcn_iglp_opt(3);
     floatx4_t sh[KH][NT][2];
     pf_prio_mfma();
 #pragma unroll
