@@ -212,15 +212,20 @@ def test_general_shapes(pka, shape):
     assert_parity(out, oracle_prefill(step), dtype, f"prefill shape {shape}", weights_rounded=True)
 
 
-def test_long_prefill_bench_size_sampled_rows(pka):
+@pytest.mark.parametrize("heads", [(16, 8, 128, 16), (8, 4, 256, 8), (8, 4, 128, 16)],
+                         ids=["16q8kv-d128", "8q4kv-d256-b8", "8q4kv-d128"])
+def test_long_prefill_bench_size_sampled_rows(pka, heads):
     """The long-prefill workload at the size and in the launch configuration
     the benchmark times (4 chunks of 2,048 rows after 6,144 cached tokens,
     bf16, 16q/8kv, head_dim 128, workspace sized by the library), checked on
     sampled rows: both ends of every chunk, rows around query-tile (64
-    positions) boundaries, and random rows."""
+    positions) boundaries, and random rows.  Also at 8q/4kv: unsplit at head
+    size 256 (one workgroup per compute unit: 528 items are two rounds), split
+    in two at head size 128."""
+    hq, hkv, d, bs = heads
     ql, cached = [2048] * 4, [6144] * 4
-    step = W.make_prefill_step(query_lens=ql, cached_lens=cached, dtype=torch.bfloat16, num_q_heads=16,
-                               num_kv_heads=8, head_dim=128, seed=0, poison=True, write_new=False)
+    step = W.make_prefill_step(query_lens=ql, cached_lens=cached, dtype=torch.bfloat16, num_q_heads=hq,
+                               num_kv_heads=hkv, head_dim=d, block_size=bs, seed=0, poison=True, write_new=False)
     ds = DevStep(step)
     Hq, D, Hkv = step.num_q_heads, step.head_dim, step.num_kv_heads
     mcl = int(step.prefill_context_lens.max())
@@ -239,5 +244,5 @@ def test_long_prefill_bench_size_sampled_rows(pka):
         rows.update((b + torch.randint(0, 2048, (6,), generator=g)).tolist())
     rows = sorted(rows)
     ref = oracle_prefill(step, rows=rows)
-    assert_parity(out.cpu()[rows], ref[rows], step.dtype, f"long prefill bench size, {len(rows)} sampled rows",
+    assert_parity(out.cpu()[rows], ref[rows], step.dtype, f"long prefill bench size {heads}, {len(rows)} sampled rows",
                   weights_rounded=True)
