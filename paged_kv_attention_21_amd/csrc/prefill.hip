@@ -22,9 +22,10 @@
 // are shared through that XCD's L2.
 //
 // Inside a split the workgroup walks 64-key tiles, staged in LDS row-major
-// (K and V alike) from registers loaded one tile ahead; a tile's physical
-// blocks come from scalar loads of the block table, so their base addresses
-// are wavefront-uniform (scalar registers).  Each wavefront owns 32 q-rows
+// (K and V alike, pieces swizzled per row) by buffer loads that write LDS
+// directly, one tile ahead; a tile's physical blocks come from scalar loads of
+// the block table, so their base addresses are wavefront-uniform (scalar
+// registers).  Each wavefront owns 32 q-rows
 // (two 16-row MFMA tiles; 16 q-rows at head size 256).
 //
 // Products (v_mfma_f32_16x16x32, fp32 accumulate):
@@ -117,22 +118,34 @@ constexpr int kPfKeys = 64;           // keys per staged tile (two 32-key halves
 constexpr int kBufferFlags = 0x00020000;
 constexpr float kPfSlack = 8.f;       // log2 growth of a row max tolerated before rescaling
 
-// LDS tiles.  Every row (of Q, K or V) takes 288 bytes up to 128 dims (544
-// bytes at 256: the same 32 bytes of padding), and in K and V tiles the
-// 16-byte pieces of rows 8..15 (mod 16) sit at piece index XOR 8.  Measured on gfx950 (bank-conflict counters of single
-// wavefronts), this is the layout where the three read patterns of the kernel
-// - K rows as the MFMA A operand, Q rows as the B operand, and the
-// transposing V reads - all run without bank conflicts; unpadded or
-// 16-byte-padded rows cost two to four extra cycles per read.
+// LDS tiles.  K and V rows are stored unpadded (D elements) and the 16-byte
+// pieces of row r sit at piece index XOR pf_swz<D>(r), so that one wavefront's
+// direct load (64 lanes x 16 bytes, written to 1 KB of consecutive LDS) fills
+// whole rows.  gfx950's LDS serves a 16-byte read eight lanes per cycle and an
+// 8-byte read sixteen lanes per cycle, from 64 four-byte banks; the swizzle
+// spreads both read patterns of the kernel over distinct banks:
+//  * K rows as the MFMA A operand: the eight lanes of a cycle read rows
+//    {0, 1, 2, 3, 8, 9, 10, 11} (+ 16, + 4) at one piece index, so the eight
+//    rows need distinct swizzles modulo 16 pieces;
+//  * transposing V reads: the sixteen lanes of a cycle read rows
+//    8 g + {0, 1, 2, 3} (+ 4), four lanes per row on a pair of adjacent
+//    pieces, so the rows need distinct swizzles once halved.
+// At 128 and 256 dims (16 or more pieces per row) the swizzle takes row bits
+// 0, 1 to piece bits 1, 2 and row bit 3 to piece bit 3.  At 64 dims (eight
+// pieces, two rows per 256 bytes) row bit 0 already picks the bank half, and
+// the swizzle takes row bits 1 and 3 to piece bits 1 and 2.  Row bit 2 is
+// left out, so K rows r and r + 4 share a swizzle.
 template <int D>
 struct PfLds {
   static_assert(D == 64 || D == 128 || D == 256, "supported head sizes");
-  static constexpr int ROW = D == 256 ? 272 : 144;  // row stride in elements
+  static constexpr int ROW = D;               // row stride in elements
   static constexpr int TILE = kPfKeys * ROW;  // one [64 keys][D] tile
   static constexpr int STAGE = 2 * TILE;      // K tile, then V tile
 };
-// Piece swizzle of K/V row `row`: 8 when bit 3 of the row is set.
-__device__ __forceinline__ int pf_swz(int row) { return (row & 8); }
+template <int D>
+__device__ __forceinline__ int pf_swz(int row) {
+  return D == 64 ? (row & 2) | ((row >> 1) & 4) : ((row & 3) << 1) | (row & 8);
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
 // output lane i gets element i % 4 of the 8-byte pieces read by input lanes
@@ -145,6 +158,12 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   const auto r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) short4v*)(const_cast<uint16_t*>(p)));
   return __builtin_bit_cast(uint2, r);
+}
+
+// Direct load of 16 bytes per lane from a buffer into LDS: lane i's bytes
+// land at `lds` + 16 i (the LDS base is wavefront-uniform).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint16_t* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
 // Bytes of one split's saved state: O[128][D], then row max[128], exp-sum[128] (fp32).
@@ -420,9 +439,13 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int THREADS = PfGeom<D>::THREADS;
   constexpr int KH = kPfKeys / 32;    // 32-key halves of a key tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LD::STAGE];  // two stages of (K, V) tiles
-  static_assert((4 * kPfOrderMaxSeqs + 1 + 2 * kPfOrderMaxTiles + kPfOrderBuckets + THREADS) * 4 <= sizeof(lds),
-                "ordering scratch");
+  // Two stages of (K, V) tiles, as two arrays: the compiler can then see that
+  // the direct loads into one stage do not touch the stage being read, and
+  // issues no wait for them before those reads.  The item ordering uses stage
+  // 0's memory first.
+  constexpr int kOrderElems = (4 * kPfOrderMaxSeqs + 1 + 2 * kPfOrderMaxTiles + kPfOrderBuckets + THREADS) * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds0[std::max(LD::STAGE, kOrderElems)];
+  __shared__ __attribute__((aligned(16))) uint16_t lds1[LD::STAGE];
 
   const int kvh = blockIdx.x;
   // Grid row blockIdx.y is an item rank: heavy-first when the batch is small
@@ -434,7 +457,7 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (num_seqs <= kPfOrderMaxSeqs && (int)gridDim.y / max(max_splits, 1) <= kPfOrderMaxTiles) {
     // (gridDim.y / max_splits bounds the batch's query tiles.)
     if (!pf_pick_item<THREADS>(query_start_loc, context_lens, num_seqs, BQ, split_keys, (int)blockIdx.y,
-                               reinterpret_cast<int*>(lds), pick_res, &tl, &split))
+                               reinterpret_cast<int*>(lds0), pick_res, &tl, &split))
       return;
   } else {
     split = (int)blockIdx.y % max_splits;
@@ -474,58 +497,59 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
-  // ---- global -> register -> LDS staging of one key tile ----
-  // Thread t moves 16-byte piece t % (D/8) of tile rows t / (D/8) + r * (THREADS / (D/8)),
-  // r < PER, for K and for V alike.  A wavefront's 64 / (D/8) rows of one
-  // pass never straddle a KV block, so the block is wavefront-uniform: its
-  // base address sits in scalar registers and each load adds a per-lane
-  // 32-bit offset.
-  constexpr int CHUNKS = kPfKeys * D / 8;             // 16-byte pieces per tile
-  // With more threads than pieces the upper threads move nothing.
-  constexpr int PER = CHUNKS >= THREADS ? CHUNKS / THREADS : 1;
-  static_assert(CHUNKS % THREADS == 0 || THREADS % CHUNKS == 0, "whole passes over the tile");
-  constexpr int ROWS_PER_PASS = THREADS / (D / 8);
-  static_assert(BS % (kWave / (D / 8)) == 0, "a wavefront's rows of one pass lie in one KV block");
-  const bool mover = CHUNKS >= THREADS || (int)threadIdx.x < CHUNKS;
-  uint4 kreg[PER], vreg[PER];                         // the next tile, on its way to LDS
-  const int my_row = threadIdx.x / (D / 8);           // row of pass 0
-  const int my_col = (threadIdx.x % (D / 8)) * 8;     // first element of the piece
+  // ---- global -> LDS staging of one key tile (direct loads) ----
+  // Every 16-byte piece goes from memory straight into LDS: a buffer load that
+  // writes LDS puts lane i's 16 bytes at the wavefront's LDS base + 16 i.
+  // Wavefront w's r-th load covers the RPI = 64 / (D/8) consecutive tile rows
+  // from RPI w + r ROWS_PER_PASS; lane i fills piece slot i % (D/8) of row
+  // i / (D/8), so it loads that row's global piece slot ^ pf_swz(row).  A
+  // wavefront's rows of one load never straddle a KV block, so the block is
+  // wavefront-uniform: its base address sits in a buffer descriptor (scalar
+  // registers) and each load adds the lane's constant 32-bit offset.
+  constexpr int PPR = D / 8;                // 16-byte pieces per row
+  constexpr int RPI = kWave / PPR;          // rows per wavefront load
+  constexpr int CHUNKS = kPfKeys * PPR;     // pieces per tile
+  static_assert(CHUNKS % THREADS == 0, "whole passes over the tile");
+  constexpr int PER = CHUNKS / THREADS;     // loads per wavefront, tile and cache
+  constexpr int ROWS_PER_PASS = THREADS / PPR;
+  static_assert(BS % RPI == 0, "a wavefront's rows of one load lie in one KV block");
+  const int my_row = threadIdx.x / PPR;     // row of pass 0
+  const int my_slot = threadIdx.x % PPR;    // LDS piece slot this lane fills
   const size_t blk_elems = (size_t)BS * row_elems;
   // A block past the context is replaced by the context's last block (only
-  // table entries inside the context are read): its rows are fetched from
-  // memory the sequence owns and then zeroed.
+  // table entries inside the context are read): its rows come from memory the
+  // sequence owns; V rows past the context are then zeroed, K rows there are
+  // masked out of the scores.
 
-  // Rows of key tile `tile` of one cache (K or V) into registers.  The
-  // physical blocks come from the block table through scalar loads; each
-  // block's base address goes into a buffer descriptor, so every lane's load
-  // is the descriptor plus its own constant byte offset and no per-lane
-  // address arithmetic is left in the loop.  K and V of one tile use the same
-  // blocks: the offsets are formed once per tile.
+  // The physical blocks come from the block table through scalar loads; each
+  // block's base address goes into a buffer descriptor.  K and V of one tile
+  // use the same blocks and the same lane offsets.
   const int32_t* __restrict__ tbl_row = block_tables + (size_t)tl.seq * max_blocks_per_seq;
   const int lb_last = (ctx - 1) / BS;  // last logical block inside the context
   // Byte offset of pass r's piece inside its block (the row's offset in the
-  // block, then the head and the dims).
+  // block, then the head and the swizzled piece).
   uint32_t goff_bytes[PER];
 #pragma unroll
-  for (int r = 0; r < PER; ++r)
-    goff_bytes[r] = (uint32_t)((((my_row + r * ROWS_PER_PASS) % BS) * row_elems + (size_t)kvh * D + my_col) * 2);
+  for (int r = 0; r < PER; ++r) {
+    const int row = my_row + r * ROWS_PER_PASS;
+    goff_bytes[r] = (uint32_t)(((row % BS) * row_elems + (size_t)kvh * D + 8 * (my_slot ^ pf_swz<D>(row))) * 2);
+  }
   const uint32_t blk_bytes = (uint32_t)(blk_elems * 2);
-  // Physical blocks of this wavefront's passes over key tile `tile` (scalar
-  // loads, issued a step before the fetch that uses them so their latency is
+  // Physical blocks of this wavefront's loads of key tile `tile` (scalar
+  // loads, issued a step before the loads that use them so their latency is
   // hidden behind a whole tile of work).
   auto lookup = [&](int tile, uint32_t (&pb)[PER]) {
     const int lb0 = (k_lo + tile * kPfKeys) / BS;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      // KV block of this pass inside the tile: the same for the whole
+      // KV block of this load inside the tile: the same for the whole
       // wavefront, so it follows from the scalar wavefront index alone.
-      const int blk_of = (wave * (kWave / (D / 8)) + r * ROWS_PER_PASS) / BS;
+      const int blk_of = (wave * RPI + r * ROWS_PER_PASS) / BS;
       pb[r] = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
     }
   };
-  auto fetch = [&](int tile, const uint32_t (&pb)[PER]) {
-    if (!mover) return;  // whole wavefronts (rows past the tile)
-    const int k0 = k_lo + tile * kPfKeys;
+  // Key tile `tile` of K and V into the stage at (kdst, vdst).
+  auto load_tile = [&](const uint32_t (&pb)[PER], uint16_t* kdst, uint16_t* vdst) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
       const uint64_t off = (uint64_t)pb[r] * blk_bytes;
@@ -533,24 +557,21 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
           const_cast<char*>(reinterpret_cast<const char*>(k_cache) + off), (short)0, 0x7fffffff, kBufferFlags);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char*>(reinterpret_cast<const char*>(v_cache) + off), (short)0, 0x7fffffff, kBufferFlags);
-      kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, goff_bytes[r], 0, 0));
-      vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, goff_bytes[r], 0, 0));
-    }
-    if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
-#pragma unroll
-      for (int r = 0; r < PER; ++r)
-        if (k0 + my_row + r * ROWS_PER_PASS >= ctx) kreg[r] = vreg[r] = make_uint4(0, 0, 0, 0);
+      const int row0 = wave * RPI + r * ROWS_PER_PASS;  // the load's first row (wavefront-uniform)
+      lds_load16(kr, kdst + row0 * LD::ROW, goff_bytes[r]);
+      lds_load16(vr, vdst + row0 * LD::ROW, goff_bytes[r]);
     }
   };
-
-  auto stage = [&](uint16_t* kdst, uint16_t* vdst) {
-    if (!mover) return;
+  // Once this wavefront's loads of key tile `tile` have landed (vmcnt 0):
+  // zero its V pieces of rows past the context, each lane the piece it loaded.
+  auto finish_tile = [&](int tile, uint16_t* vdst) {
+    const int k0 = k_lo + tile * kPfKeys;
+    if (k0 + kPfKeys > ctx) {  // the context ends inside this tile
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int row = my_row + r * ROWS_PER_PASS;
-      const int at = row * LD::ROW + (((my_col >> 3) ^ pf_swz(row)) << 3);
-      *reinterpret_cast<uint4*>(kdst + at) = kreg[r];
-      *reinterpret_cast<uint4*>(vdst + at) = vreg[r];
+      for (int r = 0; r < PER; ++r) {
+        const int row = my_row + r * ROWS_PER_PASS;
+        if (k0 + row >= ctx) *reinterpret_cast<uint4*>(vdst + row * LD::ROW + 8 * my_slot) = make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -566,10 +587,10 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // K row read by this lane in key quarter kt of a 32-key half: key
   // 8*(l16/4) + 4*kt + l16%4 of the half; its pieces 4s + blk are swizzled by
-  // ksw (the half's base row is a multiple of 32, so the swizzle bit is that
-  // of the row inside the half).
+  // ksw (the half's base row is a multiple of 32 and the swizzle leaves out
+  // row bit 2, so both key quarters and both halves share it).
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
-  const int ksw = pf_swz(krow0);  // 0 or 8, the same for both key quarters
+  const int ksw = pf_swz<D>(krow0);
 
   auto qk = [&](const uint16_t* ks, floatx4_t (&sacc)[NT][2]) {
     // S^T = K Q^T over one 32-key half and both q-row tiles.
@@ -654,16 +675,15 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto pv = [&](const uint16_t* vs, const uint4 (&pf)[NT]) {
     // O^T += V^T P^T over one 32-key half; the V^T operand (dims 16 dt + l16,
     // keys 8 blk .. +7) comes from the row-major V tile through two
-    // transposing reads.  Rows 8 blk + l16/4 (+4 for the upper half):
-    // swizzled when blk is odd, which moves each 128-dim group's dims 0..63
-    // up by 64 elements and its dims 64..127 down by 64.
-    const int vsw = (blk & 1) * 64;
-    const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 4 * (l16 & 3);
-    const uint16_t* vlo = vrd + vsw;   // dim tiles 0..3 (mod 8)
-    const uint16_t* vhi = vrd - vsw;   // dim tiles 4..7 (mod 8)
+    // transposing reads.  This lane reads rows 8 blk + l16/4 (+4 for the
+    // upper half: the same swizzle), dims 16 dt + 4 (l16 % 4) .. +3, i.e.
+    // piece 2 dt + (l16 % 4) / 2 at element 4 (l16 % 2).  The swizzle is
+    // even, so the swizzled piece is 2 (dt ^ vh) + (l16 % 4) / 2.
+    const int vh = pf_swz<D>(8 * blk + (l16 >> 2)) >> 1;
+    const uint16_t* vrd = vs + (8 * blk + (l16 >> 2)) * LD::ROW + 8 * ((l16 & 3) >> 1) + 4 * (l16 & 1);
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      const uint16_t* vp = ((dt & 4) ? vhi : vlo) + 16 * dt;
+      const uint16_t* vp = vrd + 16 * (dt ^ vh);
       const uint2 lo = lds_read_tr16(vp);
       const uint2 hi = lds_read_tr16(vp + 4 * LD::ROW);
       const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -673,30 +693,34 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
 
   // Key tiles of 64 keys, double-buffered in LDS, one barrier per tile.  Step
-  // t computes on tile t (both halves) while tile t+1 - fetched into
-  // registers during step t-1 - is written to the other buffer and tile t+2
-  // is fetched: every global load has a whole step to land.  Within the step
-  // the two halves are interleaved so the softmax of one half can overlap
-  // the MFMAs of the other: S of both halves, then softmax + PV of half 0,
-  // then softmax + PV of half 1.  Fetch indices are clamped at the last tile,
-  // so every wave issues the same loads on every path and each wait stays
-  // exact.
+  // t computes on tile t (both halves) while tile t+1 loads straight into the
+  // other stage (free since the last barrier): the loads have the whole step
+  // to land, and each wavefront waits for its own before the barrier that
+  // hands the tile to the others.  Within the step the two halves are
+  // interleaved so the softmax of one half can overlap the MFMAs of the
+  // other: S of both halves, then softmax + PV of half 0, then softmax + PV
+  // of half 1.
   const int last_tile = ntiles - 1;
-  uint32_t pb_next[PER];  // blocks of the tile the next step fetches
+  uint32_t pb_next[PER];  // blocks of the tile the next step loads
   if (ntiles > 0) {
     uint32_t pb0[PER];
     lookup(0, pb0);
     lookup(min(1, last_tile), pb_next);
-    fetch(0, pb0);
-    stage(lds, lds + LD::TILE);
-    fetch(min(1, last_tile), pb_next);
-    lookup(min(2, last_tile), pb_next);
+    load_tile(pb0, lds0, lds0 + LD::TILE);
+    __builtin_amdgcn_s_waitcnt(0);
+    finish_tile(0, lds0 + LD::TILE);
     __syncthreads();
   }
-  for (int t = 0; t < ntiles; ++t) {
-    const uint16_t* kt_lds = lds + (t & 1) * LD::STAGE;
+  // (The stage pointers are restrict: once inlined, that tells the compiler
+  // the direct loads into `next` do not alias the reads of `kt_lds`.)
+  auto step = [&](int t, const uint16_t* __restrict__ kt_lds, uint16_t* __restrict__ next)
+                  __attribute__((always_inline)) {
     const uint16_t* vt_lds = kt_lds + LD::TILE;
-    uint16_t* next = lds + ((t + 1) & 1) * LD::STAGE;
+    const bool more = t < last_tile;  // wavefront-uniform
+    if (more) {
+      load_tile(pb_next, next, next + LD::TILE);
+      lookup(min(t + 2, last_tile), pb_next);
+    }
     // Scheduler hint: interleave the tile's MFMAs with its exp work (the
     // compiler's strategy for softmax-between-products loops).  Measured:
     // long prefill 1,012 -> 1,019-1,021 TFLOP/s, mixed-step prefill call
@@ -707,11 +731,6 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int h = 0; h < KH; ++h) qk(kt_lds + h * 32 * LD::ROW, sh[h]);
     pf_prio_valu();
-    // Tile t+1 into the buffer tile t-1 used (free since the last barrier),
-    // then tile t+2 into the registers.
-    stage(next, next + LD::TILE);
-    fetch(min(t + 2, last_tile), pb_next);
-    lookup(min(t + 3, last_tile), pb_next);
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
       uint4 pf[NT];
@@ -721,7 +740,16 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pv(vt_lds + h * 32 * LD::ROW, pf);
       pf_prio_valu();
     }
+    // This wavefront's loads have landed (unconditional, so no load counts as
+    // outstanding into the next step on any path).
+    __builtin_amdgcn_s_waitcnt(0);
+    if (more) finish_tile(t + 1, next + LD::TILE);
     __syncthreads();
+  };
+  // Even tiles sit in stage 0, odd tiles in stage 1.
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, lds0, lds1);
+    if (t + 1 < ntiles) step(t + 1, lds1, lds0);
   }
 
   // Lane holds dims 16*dt + 4*blk + i of q-row l16 of tile nt.
