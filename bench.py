@@ -60,8 +60,8 @@ TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
     "decode_step": ("decode_impl.h", "6896da5d79401c76", 1191836812),
     "splitk": ("decode_impl.h", "6896da5d79401c76", 269528730),
-    "mixed": ("prefill.hip", "7f7abc95da5b1821", 50250968),
-    "prefill_long": ("prefill.hip", "7f7abc95da5b1821", 464939456),
+    "mixed": ("prefill.hip", "5d04b52a5d55f372", 50250969),
+    "prefill_long": ("prefill.hip", "5d04b52a5d55f372", 465283440),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),
 }
 

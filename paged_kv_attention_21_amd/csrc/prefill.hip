@@ -548,7 +548,8 @@ paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pb[r] = (uint32_t)tbl_row[min(lb0 + blk_of, lb_last)];
     }
   };
-  // Key tile `tile` of K and V into the stage at (kdst, vdst).
+  // The K and V rows of the key tile whose blocks `lookup` put in `pb`, into
+  // the stage at (kdst, vdst).
   auto load_tile = [&](const uint32_t (&pb)[PER], uint16_t* kdst, uint16_t* vdst) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
