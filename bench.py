@@ -58,8 +58,8 @@ ROPE_THETA = 1e6               # rotary base of the rope_kv_write workload (Qwen
 # source of its traffic figure, or why it is null.
 TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
-    "decode_step": ("decode_impl.h", "6896da5d79401c76", 1191836812),
-    "splitk": ("decode_impl.h", "6896da5d79401c76", 269528730),
+    "decode_step": ("decode_impl.h", "508287ea44944b78", 1191837382),
+    "splitk": ("decode_impl.h", "508287ea44944b78", 269528776),
     "mixed": ("prefill.hip", "5d04b52a5d55f372", 50250969),
     "prefill_long": ("prefill.hip", "5d04b52a5d55f372", 465283440),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),

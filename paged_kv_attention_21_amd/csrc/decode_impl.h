@@ -162,8 +162,12 @@ struct McGeom {
   // Register buffers of the load ring (8 * NL registers each): while one
   // unit is computed, the next one's loads are in flight.  Two: measured at
   // 64 dims, rings of three and four cost occupancy (three and four
-  // wavefronts per SIMD against four) and ran 2-4 % slower.
-  static constexpr int RING = 2;
+  // wavefronts per SIMD against four) and ran 2-4 % slower.  One at 256 dims,
+  // where a wavefront already holds the whole register file (one per SIMD):
+  // a second unit's 64 registers made the partition-only form with 32-token
+  // blocks spill, and measured no faster (group 8, 32-token blocks: 206.7
+  // against 208.2 us).
+  static constexpr int RING = D == 256 ? 1 : 2;
 };
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
