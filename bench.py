@@ -60,8 +60,8 @@ TRAFFIC_PROFILE = "profiles/traffic_fetch_write.md"
 RECORDED_TRAFFIC = {
     "decode_step": ("decode_impl.h", "508287ea44944b78", 1191837382),
     "splitk": ("decode_impl.h", "508287ea44944b78", 269528776),
-    "mixed": ("prefill.hip", "5d04b52a5d55f372", 50250969),
-    "prefill_long": ("prefill.hip", "5d04b52a5d55f372", 465283440),
+    "mixed": ("prefill.hip", "0f354d6425638b9e", 50251018),
+    "prefill_long": ("prefill.hip", "0f354d6425638b9e", 465589472),
     "rope_kv_write": ("rope_kv.hip", "6db5d8adbcf54e98", 34923040),
 }
 

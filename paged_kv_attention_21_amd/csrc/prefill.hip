@@ -246,7 +246,9 @@ __device__ __forceinline__ bool pf_tile(const int32_t* __restrict__ qsl, const i
 // context_lens, in LDS scratch that the key tiles later overwrite.
 constexpr int kPfOrderBuckets = kWave;
 constexpr int kPfOrderMaxSeqs = 256;    // chunks the ordering handles; above, grid order is kept
-constexpr int kPfOrderMaxTiles = 4096;  // query tiles likewise
+// Query tiles likewise.  3,584 keeps the scratch (34 KB) within what a
+// head-size-64 workgroup may take for three to share a compute unit.
+constexpr int kPfOrderMaxTiles = 3584;
 
 // Finds the item of rank `rank` and fills *t (as pf_tile) and *split; false
 // when the batch has fewer items.  scratch: LDS for (4 kPfOrderMaxSeqs + 1 +
@@ -418,9 +420,17 @@ __device__ bool pf_pick_item(const int32_t* __restrict__ qsl, const int32_t* __r
   return true;
 }
 
+// Wavefronts per SIMD the kernel is compiled for: two (a workgroup of four
+// takes up to 200 registers a lane and 66 KB of LDS at head size 128, 128 KB
+// at 256), three at head size 64 (136 registers, 50 KB: three workgroups per
+// compute unit; measured 785 -> 872 TFLOP/s on the long prefill's chunks).
+template <int D>
+constexpr int pf_waves_per_simd() { return D == 64 ? 3 : 2; }
+
 // BS = tokens per KV block (8, 16 or 32): a 64-key tile spans 64 / BS blocks.
 template <typename T, int D, int G, int BS>
-__global__ void __launch_bounds__(PfGeom<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(PfGeom<D>::THREADS)
+    __attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<D>(), pf_waves_per_simd<D>())))
 paged_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                      const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,

@@ -63,6 +63,21 @@ def test_ragged_chunks(pka, shape):
     assert_parity(out, oracle_prefill(step), dtype, f"ragged prefill {shape}", weights_rounded=True)
 
 
+def test_many_chunks_grid_order(pka):
+    """More chunks (300) than the kernel's heavy-first item ordering takes
+    (256): every workgroup falls back to grid order (query tile, split) and
+    the batch must still be covered exactly once.  Chunks of 1-40 rows after
+    0-300 cached tokens, so their ends fall anywhere inside KV blocks and key
+    tiles."""
+    ql = [1 + (7 * i) % 40 for i in range(300)]
+    cl = [(37 * i) % 301 for i in range(300)]
+    step = W.make_prefill_step(query_lens=ql, cached_lens=cl, dtype=torch.bfloat16, num_q_heads=16, num_kv_heads=8,
+                               head_dim=128, seed=38, poison=True, write_new=False)
+    ds = DevStep(step)
+    out = run_prefill(pka, ds)
+    assert_parity(out, oracle_prefill(step), step.dtype, "300-chunk prefill (grid order)", weights_rounded=True)
+
+
 @pytest.mark.parametrize("shape", [(torch.bfloat16, 16, 8, 128), (torch.float16, 8, 8, 64)],
                          ids=["bf16-16q8kv-d128", "fp16-8q8kv-d64"])
 def test_long_context_splits(pka, shape):
