@@ -224,6 +224,9 @@ GENERAL = [
     (torch.bfloat16, 32, 4, 128, 32),
     (torch.float16, 16, 2, 256, 32),
     (torch.bfloat16, 8, 4, 256, 32),
+    # group 4 at head size 256 with 32-slot blocks, bf16 (one unit in flight
+    # on the matrix cores; the partition-only form under v2)
+    (torch.bfloat16, 32, 8, 256, 32),
 ]
 
 
